@@ -1,0 +1,321 @@
+"""Pins for the fp64 CPU oracle: closed forms, hand-derived values and invariants.
+
+None of these re-types the oracle's formula: each compares it with something
+the pages and the mathematics fix independently, so a dropped term, a wrong
+sign, a swapped axis or a wrong smoothing constant fails at least one test.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from direct_coulomb_potential_amd.workloads import random_atoms
+
+
+def _lin(ijk, dims):
+    i, j, k = ijk
+    return (k * dims[1] + j) * dims[0] + i
+
+
+def _eval_expr(s):
+    # fixture values are tiny expressions: rationals and sqrt of integers
+    return float(eval(s, {"__builtins__": {}}, {"sqrt": math.sqrt}))
+
+
+# ---------------------------------------------------------------- direct sum
+
+def test_direct_golden_single_atom(golden_dir):
+    """Exact q/r at hand-picked nodes (page 1, sections 18.1 and 18.2)."""
+    with open(os.path.join(golden_dir, "direct_single_atom.json")) as f:
+        fx = json.load(f)
+    for case in fx["cases"]:
+        dims = case["dims"]
+        atoms = np.array(case["atoms"], dtype=np.float32)
+        nodes = np.array([_lin(n["ijk"], dims) for n in case["nodes"]], dtype=np.int64)
+        V = oracle.direct(atoms, dims, case["spacing"], case["origin"], nodes=nodes)
+        want = np.array([_eval_expr(n["V"]) for n in case["nodes"]])
+        np.testing.assert_allclose(V, want, rtol=1e-15, atol=0, err_msg=case["note"])
+        # the whole-lattice call stores the same values at the same linear indices
+        Vall = oracle.direct(atoms, dims, case["spacing"], case["origin"])
+        np.testing.assert_allclose(Vall[nodes], want, rtol=1e-15, atol=0)
+
+
+def test_direct_node_is_one_fp32_rounding_of_origin_plus_ih():
+    """Reading R1: node x = fl32(o + i*h).  With h = 0.1f, i = 3 the exact
+    3*0.1f = 0.300000004470348... rounds to 0.3f = 0.300000011920929; an atom
+    placed at exactly that fp32 x and 2^-20 away in y must see r = 2^-20."""
+    h = np.float32(0.1)
+    x3 = np.float32(0.3)
+    assert float(x3) != 3 * float(h)
+    atoms = np.array([[x3, 2.0 ** -20, 0.0, 1.0]], dtype=np.float32)
+    V = oracle.direct(atoms, (4, 1, 1), h, (0.0, 0.0, 0.0), nodes=np.array([3]))
+    assert V[0] == 2.0 ** 20
+
+
+def test_direct_symmetric_shells_closed_form():
+    """Charges on the 6 axis points and 8 cube corners around one node: V is
+    6q1/R + 8q2/(s*sqrt(3)); any dropped coordinate or sign error breaks it."""
+    R, s, q1, q2 = 1.5, 0.75, 0.625, -0.25
+    c = np.array([2.0, 3.0, 4.0])  # node (4, 6, 8) of an h = 0.5 lattice
+    pts = []
+    for ax in range(3):
+        for sg in (-1, 1):
+            p = c.copy()
+            p[ax] += sg * R
+            pts.append([*p, q1])
+    for sx in (-1, 1):
+        for sy in (-1, 1):
+            for sz in (-1, 1):
+                pts.append([c[0] + sx * s, c[1] + sy * s, c[2] + sz * s, q2])
+    atoms = np.array(pts, dtype=np.float32)
+    dims = (9, 13, 17)
+    V = oracle.direct(atoms, dims, 0.5, (0, 0, 0), nodes=np.array([_lin((4, 6, 8), dims)]))
+    want = 6 * q1 / R + 8 * q2 / (s * math.sqrt(3.0))
+    assert V[0] == pytest.approx(want, rel=1e-14)
+
+
+def test_direct_superposition_and_linearity():
+    """V is linear in the charges and additive over atom sets."""
+    A = random_atoms(37, (-2, -2, -2), (6, 5, 7), seed=11)
+    B = random_atoms(29, (0, 0, 0), (4, 4, 4), seed=12)
+    dims, h, o = (7, 6, 5), 0.75, (-0.5, 0.25, 0.0)
+    VA = oracle.direct(A, dims, h, o)
+    VB = oracle.direct(B, dims, h, o)
+    VAB = oracle.direct(np.concatenate([A, B]), dims, h, o)
+    np.testing.assert_allclose(VAB, VA + VB, rtol=1e-12, atol=1e-12)
+    A2 = A.copy()
+    A2[:, 3] *= np.float32(-2.0)
+    np.testing.assert_allclose(oracle.direct(A2, dims, h, o), -2.0 * VA, rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("axis", [0, 1, 2])
+def test_direct_mirror_symmetry(axis):
+    """Atoms mirrored through the lattice mid-plane: equal charges give
+    V(i) = V(n-1-i) along that axis; opposite charges give V = 0 on the
+    mid-plane (n odd).  Dyadic coordinates keep the mirror exact in fp32."""
+    dims = [7, 9, 5]
+    dims[axis] = 11
+    h = 0.5
+    mid = (dims[axis] - 1) * h / 2.0
+    rng = np.random.default_rng(100 + axis)
+    n = 20
+    pos = np.round(rng.uniform(-1.0, 6.0, size=(n, 3)) * 64) / 64 + 1.0 / 128
+    mirrored = pos.copy()
+    mirrored[:, axis] = 2 * mid - pos[:, axis]
+    q = np.round(rng.uniform(-1, 1, size=n) * 256) / 256
+    same = np.concatenate([np.c_[pos, q], np.c_[mirrored, q]]).astype(np.float32)
+    opp = np.concatenate([np.c_[pos, q], np.c_[mirrored, -q]]).astype(np.float32)
+    Vs = oracle.direct(same, dims, h).reshape(dims[2], dims[1], dims[0])
+    Vo, So = oracle.direct(opp, dims, h, with_scale=True)
+    Vo = Vo.reshape(dims[2], dims[1], dims[0])
+    So = So.reshape(dims[2], dims[1], dims[0])
+    np_axis = 2 - axis  # array axes are (k, j, i)
+    np.testing.assert_allclose(Vs, np.flip(Vs, axis=np_axis), rtol=1e-12, atol=1e-12)
+    mid_index = dims[axis] // 2
+    plane = np.take(Vo, mid_index, axis=np_axis)
+    scale = np.take(So, mid_index, axis=np_axis)
+    assert np.all(np.abs(plane) <= 1e-13 * scale)
+    assert np.all(scale > 0)
+
+
+def test_direct_translation_invariance():
+    """Shifting atoms and lattice origin by whole spacings leaves V unchanged."""
+    h = 0.5
+    A = random_atoms(50, (0, 0, 0), (4, 4, 4), seed=21)
+    A[:, :3] = np.round(A[:, :3] * 64) / 64 + 1.0 / 256
+    dims = (8, 8, 8)
+    V0 = oracle.direct(A, dims, h, (0.0, 0.0, 0.0))
+    shift = np.array([3 * h, -2 * h, 5 * h], dtype=np.float32)
+    B = A.copy()
+    B[:, :3] += shift
+    V1 = oracle.direct(B, dims, h, tuple(float(s) for s in shift))
+    np.testing.assert_allclose(V1, V0, rtol=1e-13, atol=1e-13)
+
+
+def test_direct_far_field_of_a_dipole():
+    """A neutral pair (+q at +d/2, -q at -d/2 along x) seen from far along x:
+    V -> q d / x^2 (dipole closed form); the next term is O((d/x)^2)."""
+    d, q = 0.5, 0.8
+    atoms = np.array([[d / 2, 0, 0, q], [-d / 2, 0, 0, -q]], dtype=np.float32)
+    x = 400.0
+    V = oracle.direct(atoms, (1, 1, 1), 1.0, (x, 0.0, 0.0))
+    assert V[0] == pytest.approx(q * d / x**2, rel=1e-5)
+
+
+def test_direct_scale_is_sum_of_magnitudes():
+    """S = sum |q|/r: equal to V when all charges are positive, and to V of the
+    |q| set in general."""
+    A = random_atoms(40, (-1, -1, -1), (5, 5, 5), seed=31)
+    dims, h = (6, 5, 4), 1.0
+    V, S = oracle.direct(A, dims, h, with_scale=True)
+    Aabs = A.copy()
+    Aabs[:, 3] = np.abs(Aabs[:, 3])
+    Vabs, Sabs = oracle.direct(Aabs, dims, h, with_scale=True)
+    np.testing.assert_allclose(S, Vabs, rtol=1e-14)
+    np.testing.assert_allclose(Sabs, Vabs, rtol=1e-14)
+    assert np.all(np.abs(V) <= S * (1 + 1e-14))
+
+
+def test_direct_node_subset_matches_full_lattice():
+    A = random_atoms(30, (0, 0, 0), (3, 3, 3), seed=41)
+    dims = (5, 4, 3)
+    full = oracle.direct(A, dims, 0.75, (0.1, 0.2, 0.3))
+    nodes = np.array([59, 0, 17, 33, 17], dtype=np.int64)
+    sub = oracle.direct(A, dims, 0.75, (0.1, 0.2, 0.3), nodes=nodes)
+    assert np.array_equal(sub, full[nodes])
+
+
+def test_direct_no_atoms_is_zero():
+    V, S = oracle.direct(np.zeros((0, 4), np.float32), (3, 2, 2), 0.5, with_scale=True)
+    assert np.all(V == 0) and np.all(S == 0)
+
+
+# ---------------------------------------------------------------- smoothed cutoff
+
+def test_smoothed_term_golden(golden_dir):
+    """Hand-derived values of q (1/r - gamma(r^2)) (binning lecture, slide 24)."""
+    with open(os.path.join(golden_dir, "smoothed_term.json")) as f:
+        fx = json.load(f)
+    for c in fx["cases"]:
+        got = oracle.smoothed_term(c["q"], c["r"], c["rc"])
+        want = _eval_expr(c["value"])
+        assert got == pytest.approx(want, rel=1e-13, abs=0), c
+    # 53/128 and 4509/2048 are the polynomial at u = 1/2 and 1/4, by hand:
+    u = Fraction(1, 2)
+    assert 1 / u - Fraction(15, 8) + Fraction(5, 4) * u**2 - Fraction(3, 8) * u**4 == Fraction(53, 128)
+
+
+def test_smoothed_term_vanishes_to_third_order_at_rc(golden_dir):
+    """gamma matches 1/r in value, slope and curvature at rc, so the term
+    behaves like (2.5 d^3 + 0.625 d^4 + d^5)/rc at r = rc (1 - d)."""
+    with open(os.path.join(golden_dir, "smoothed_term.json")) as f:
+        tay = json.load(f)["taylor_near_rc"]
+    rc = tay["rc"]
+    for d in tay["deltas"]:
+        got = oracle.smoothed_term(1.0, rc * (1 - d), rc)
+        series = (2.5 * d**3 + 0.625 * d**4 + d**5) / rc
+        assert got == pytest.approx(series, rel=2 * d**2 + 1e-9), d
+    assert oracle.smoothed_term(1.0, rc, rc) == 0.0
+    assert oracle.smoothed_term(1.0, rc * (1 + 1e-12), rc) == 0.0
+
+
+def test_cutoff_single_atom_matches_term_and_is_zero_outside():
+    """One atom; nodes at r = 6 (inside rc = 12) and r = 13, 12 (outside)."""
+    atoms = np.array([[0.0, 0.0, 0.0, 1.0]], dtype=np.float32)
+    dims = (1, 1, 3)
+    # nodes at z = 6, 12 (tie: excluded, term is 0 there anyway), 18
+    V, S = oracle.cutoff(atoms, dims, 6.0, (0.0, 0.0, 6.0), 12.0, with_scale=True)
+    assert V[0] == pytest.approx(53 / (128 * 12), rel=1e-14)
+    assert S[0] == pytest.approx(1 / 6, rel=1e-15)
+    assert V[1] == 0.0 and V[2] == 0.0 and S[1] == 0.0 and S[2] == 0.0
+
+
+def test_cutoff_shells_closed_form():
+    """Atoms on shells at r = 3, 6 (inside rc = 12) and 13, 20 (outside) of a
+    single node: V = sum over the inside shells of q f(r), S = sum |q|/r."""
+    c = np.array([10.0, 10.0, 10.0])
+    shells = [(3.0, 0.5), (6.0, -0.25), (13.0, 1.0), (20.0, -1.0)]
+    pts = []
+    for r, q in shells:
+        for ax in range(3):
+            for sg in (-1, 1):
+                p = c.copy()
+                p[ax] += sg * r
+                pts.append([*p, q])
+    atoms = np.array(pts, dtype=np.float32)
+    V, S = oracle.cutoff(atoms, (1, 1, 1), 1.0, tuple(c), 12.0, with_scale=True)
+    rc = 12.0
+    want = 6 * (0.5 * 4509 / (2048 * rc) - 0.25 * 53 / (128 * rc))
+    assert V[0] == pytest.approx(want, rel=1e-13)
+    assert S[0] == pytest.approx(6 * (0.5 / 3 + 0.25 / 6), rel=1e-14)
+
+
+def test_cutoff_zero_beyond_cutoff():
+    """Nodes farther than rc from every atom get exactly 0."""
+    A = random_atoms(200, (0, 0, 0), (10, 10, 10), seed=51)
+    # lattice starts at x = 22.5: every node is > 12 A from [0,10]^3
+    V, S = oracle.cutoff(A, (4, 4, 4), 1.0, (22.5, 0.0, 0.0), 12.0, with_scale=True)
+    assert np.all(V == 0.0) and np.all(S == 0.0)
+
+
+def test_cutoff_tends_to_direct_for_huge_cutoff():
+    """With rc far beyond every distance and net charge zero, the cutoff sum
+    differs from the direct sum only by gamma's r^2 and r^4 moments, which
+    are O(L^2/rc^3) for an atom set of size L."""
+    A = random_atoms(64, (0, 0, 0), (5, 5, 5), seed=61)
+    A[:, 3] -= np.float32(A[:, 3].astype(np.float64).mean())
+    q = A[:, 3].astype(np.float64)
+    dims, h = (4, 4, 4), 1.0
+    Vd = oracle.direct(A, dims, h)
+    for rc in (1.0e3, 1.0e4):
+        Vc = oracle.cutoff(A, dims, h, (0, 0, 0), rc)
+        bound = 1.25 * np.abs(q).sum() * 3 * 10.0**2 / rc**3 + 15 / (8 * rc) * abs(q.sum())
+        assert np.max(np.abs(Vc - Vd)) <= bound, rc
+
+
+def test_cutoff_positive_charges_bounded_by_direct():
+    """The term is >= 0 on (0, rc], so with q > 0: 0 <= V_cut <= V_direct."""
+    A = random_atoms(300, (0, 0, 0), (20, 20, 20), seed=71, q_lo=0.0, q_hi=1.0)
+    dims, h = (9, 9, 9), 2.5
+    Vd = oracle.direct(A, dims, h)
+    Vc = oracle.cutoff(A, dims, h, (0, 0, 0), 8.0)
+    assert np.all(Vc >= 0) and np.all(Vc <= Vd)
+    assert np.any(Vc > 0)
+
+
+# ---------------------------------------------------------------- binning
+
+def test_bin_grid_golden(golden_dir):
+    with open(os.path.join(golden_dir, "binning.json")) as f:
+        fx = json.load(f)
+    for g in fx["grids"]:
+        bins, b0, halo = oracle.bin_grid(g["dims"], g["spacing"], g["origin"], g["bin_size"], g["cutoff"])
+        assert halo == g["halo"], g["note"]
+        assert list(bins) == g["bins"], g["note"]
+        assert list(b0.astype(float)) == g["b0"], g["note"]
+
+
+def test_bin_atoms_golden(golden_dir):
+    with open(os.path.join(golden_dir, "binning.json")) as f:
+        fx = json.load(f)["atoms_in_4x4x4_bs2_rc3"]
+    atoms = np.array(fx["atoms"], dtype=np.float32)
+    starts, sorted_atoms, bin_of = oracle.bin_atoms(atoms, (4, 4, 4), 1.0, (0, 0, 0), 2.0, 3.0)
+    assert list(bin_of) == fx["bins"]
+    kept = [i for i, b in enumerate(fx["bins"]) if b >= 0]
+    assert starts[-1] == len(kept)
+    # bin 86 holds input atoms 0, 6, 8, 9 in input order
+    s, e = starts[86], starts[87]
+    np.testing.assert_array_equal(sorted_atoms[s:e], atoms[[0, 6, 8, 9]])
+
+
+def test_bin_atoms_is_a_stable_sort_with_correct_boxes():
+    """The CSR equals a stable sort by bin (numpy's stable argsort as the
+    library routine); every kept atom lies in its bin's box and every dropped
+    atom is at least rc from the lattice's bounding box."""
+    dims, h, o, bs, rc = (20, 16, 12), 0.5, (1.0, -2.0, 0.5), 1.25, 3.0
+    A = random_atoms(5000, (-4, -7, -4), (16, 8, 11), seed=81)
+    starts, srt, bin_of = oracle.bin_atoms(A, dims, h, o, bs, rc)
+    bins, b0, halo = oracle.bin_grid(dims, h, o, bs, rc)
+    nb = bins[0] * bins[1] * bins[2]
+    kept = bin_of >= 0
+    order = np.argsort(np.where(kept, bin_of, nb), kind="stable")[: kept.sum()]
+    np.testing.assert_array_equal(srt, A[order])
+    np.testing.assert_array_equal(starts, np.concatenate([[0], np.cumsum(np.bincount(bin_of[kept], minlength=nb))]))
+    # boxes (fp64 with a rounding allowance)
+    b = bin_of[kept]
+    cx, cy, cz = b % bins[0], (b // bins[0]) % bins[1], b // (bins[0] * bins[1])
+    P = A[kept, :3].astype(np.float64)
+    for ax, cc in enumerate((cx, cy, cz)):
+        lo = b0[ax] + cc * bs
+        assert np.all(P[:, ax] >= lo - 1e-5) and np.all(P[:, ax] <= lo + bs + 1e-5)
+    # dropped atoms are at least rc (up to rounding) from the lattice box
+    lat_lo = np.array(o, np.float64)
+    lat_hi = lat_lo + (np.array(dims) - 1) * h
+    D = A[~kept, :3].astype(np.float64)
+    gap = np.maximum(0, np.maximum(lat_lo - D, D - lat_hi))
+    assert np.all(np.sqrt((gap**2).sum(1)) >= rc - 1e-4)
+    assert (~kept).sum() > 0 and kept.sum() > 0
