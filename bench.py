@@ -1,0 +1,214 @@
+"""Benchmark of the potential-map hot path on one MI355X.
+
+One step = one cpmap_direct call over the 200^3 lattice (0.5 A) with 200,000
+uniform atoms (charges U[-1,1] shifted to net zero): 1.6e12 atom-node
+evaluations.  After the timed direct steps the same run times the cutoff path
+(cpmap_bin_atoms + cpmap_cutoff) on the 100k-atom, rc = 12 A, 4 A-bin system
+over the same lattice and reports it beside the headline number.
+
+Prints ONE JSON line.  `value` is atom-node evaluations per second (G/s) with
+inputs already resident in HBM; `roofline` prices the direct kernel against the
+fp32 VALU peak at 10 FLOP per evaluation; `cpu_baseline` times the fp64 oracle
+on a bounded sample of nodes on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP32_TFLOPS = 157.3   # MI355X fp32 vector peak (256 CU x 2.4 GHz x 256 FLOP/clk)
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+FLOP_PER_EVAL = 10
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="target CPU time of the oracle baseline sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-cutoff", action="store_true")
+    p.add_argument("--only", choices=["direct", "cutoff"], default=None,
+                   help="time one path only (for profiler runs)")
+    return p.parse_args()
+
+
+def time_launches(torch, fn, steps, warmup):
+    """Run fn warmup times, then `steps` times between device syncs, each launch
+    bracketed by events on torch's current stream (the stream the library
+    launches on).  Returns (wall seconds of the timed region, per-launch ms)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, [a.elapsed_time(b) for a, b in evs]
+
+
+def cpu_baseline(oracle, w, target_s):
+    """The fp64 oracle, as it stands, on a bounded node sample of the workload."""
+    lat = w.lattice
+    rng = np.random.default_rng(1234)
+    probe = rng.integers(0, lat.n_points, size=64, dtype=np.int64)
+    t0 = time.perf_counter()
+    oracle.direct(w.atoms, lat.dims, lat.spacing, lat.origin, nodes=probe)
+    rate = probe.size * w.n_atoms / max(time.perf_counter() - t0, 1e-6)
+    n_nodes = int(min(max(rate * target_s / w.n_atoms, 256), lat.n_points))
+    nodes = rng.integers(0, lat.n_points, size=n_nodes, dtype=np.int64)
+    t0 = time.perf_counter()
+    oracle.direct(w.atoms, lat.dims, lat.spacing, lat.origin, nodes=nodes)
+    dt = time.perf_counter() - t0
+    return {
+        "value": n_nodes * w.n_atoms / dt / 1e9,
+        "unit": "G evals/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{n_nodes} random nodes of the 200^3 lattice x all {w.n_atoms} atoms, fp64, "
+                  f"{dt:.1f} s",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by lattice z-slabs, one per GPU, with no exchange)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import direct_coulomb_potential_amd as cpmap
+    from direct_coulomb_potential_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    cpmap.library()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    w = wl.large_direct()
+    lat = w.lattice
+    pairs = w.pairs
+    result = {
+        "metric": "atom-gridpoint evals/sec (G/s) + % FP32 VALU peak, 200³ grid × 200k atoms",
+        "unit": "G evals/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded uniform atoms, charges U[-1,1] shifted to net zero)",
+        "config": {"workload": w.name, "lattice": list(lat.dims), "spacing": lat.spacing,
+                   "atoms": w.n_atoms, "pairs_per_step": pairs, "parallelism": "single GPU"},
+    }
+
+    if args.only in (None, "direct"):
+        atoms = torch.from_numpy(w.atoms).to(dev)
+        V = torch.empty((lat.nz, lat.ny, lat.nx), dtype=torch.float32, device=dev)
+        fn = lambda: cpmap.direct(atoms, lat, out=V)  # noqa: E731
+        wall, per = time_launches(torch, fn, args.steps, args.warmup)
+        ms_step = wall / args.steps * 1e3
+        kern_ms = statistics.mean(per)
+        achieved = FLOP_PER_EVAL * pairs / (kern_ms * 1e-3) / 1e12
+        result.update({
+            "value": pairs * args.steps / wall / 1e9,
+            "ms_per_step": ms_step,
+            "pct_fp32_valu_peak": 100.0 * FLOP_PER_EVAL * pairs / (ms_step * 1e-3) / 1e12
+            / PEAK_FP32_TFLOPS,
+        })
+        result["roofline"] = {
+            "bound": "alu",
+            "achieved": achieved,
+            "peak": PEAK_FP32_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_FP32_TFLOPS,
+            "traffic": None,
+            "kernel": "direct_kernel",
+            "kernel_ms_mean": kern_ms,
+            "kernel_ms_median": statistics.median(per),
+            "kernel_ms_min": min(per),
+            "flop_per_eval": FLOP_PER_EVAL,
+        }
+        del atoms, V
+
+    if not args.no_cutoff and args.only in (None, "cutoff"):
+        result["cutoff"] = bench_cutoff(torch, cpmap, wl, dev, args)
+
+    if not args.no_cpu_baseline and args.only is None:
+        import oracle
+        result["cpu_baseline"] = cpu_baseline(oracle, w, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+def bench_cutoff(torch, cpmap, wl, dev, args):
+    w = wl.cutoff_binned()
+    lat = w.lattice
+    atoms = torch.from_numpy(w.atoms).to(dev)
+    bs, rc = w.bin_size, w.cutoff
+    try:
+        ws = cpmap.bin_atoms(atoms, lat, bs, rc)
+        V = cpmap.cutoff(ws, w.n_atoms, lat, bs, rc)
+        torch.cuda.synchronize()
+    except cpmap.CpmapError as e:
+        return {"skipped": str(e)}
+    # L2 flush buffer (larger than the 8 x 4 MB of L2) between timed runs
+    flush = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+
+    def run_bin():
+        cpmap.bin_atoms(atoms, lat, bs, rc, workspace=ws)
+
+    def run_cut():
+        cpmap.cutoff(ws, w.n_atoms, lat, bs, rc, out=V)
+
+    def run_both():
+        flush.zero_()
+        run_bin()
+        run_cut()
+
+    steps = max(args.steps, 5)
+    _, per_bin = time_launches(torch, run_bin, steps, args.warmup)
+    _, per_cut = time_launches(torch, run_cut, steps, args.warmup)
+    wall_e2e, _ = time_launches(torch, run_both, steps, args.warmup)
+    Vd = torch.empty_like(V)
+    _, per_dir = time_launches(torch, lambda: cpmap.direct(atoms, lat, out=Vd), 2, 1)
+    cut_ms = statistics.median(per_cut)
+    bin_ms = statistics.median(per_bin)
+    dir_ms = statistics.median(per_dir)
+    bytes_alg = 16 * w.n_atoms + 4 * lat.n_points
+    return {
+        "workload": w.name,
+        "bin_ms_median": bin_ms,
+        "cutoff_ms_median": cut_ms,
+        "cutoff_ms_min": min(per_cut),
+        "end_to_end_ms_with_l2_flush": wall_e2e / steps * 1e3,
+        "direct_same_atoms_ms": dir_ms,
+        "speedup_vs_direct": dir_ms / (cut_ms + bin_ms),
+        "hbm_gbs_algorithmic": bytes_alg / (cut_ms * 1e-3) / 1e9,
+        "direct_equivalent_G_evals_per_s": w.pairs / ((cut_ms + bin_ms) * 1e-3) / 1e9,
+    }
+
+
+if __name__ == "__main__":
+    main()

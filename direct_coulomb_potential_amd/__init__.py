@@ -1,1 +1,222 @@
-"""cpmap: electrostatic potential maps on MI355X (gfx950)."""
+"""cpmap: electrostatic potential maps on AMD Instinct MI355X (gfx950).
+
+A thin binding over libcpmap.so (C ABI in include/cpmap.h).  It only checks
+and marshals arguments: every step of the computation runs in the library's
+HIP kernels.  PyTorch provides device memory and the current stream.  There
+is no CPU fallback: if libcpmap.so is missing or fails to load, every call
+raises.
+
+    import direct_coulomb_potential_amd as cpmap
+    lat = cpmap.Lattice(200, 200, 200, 0.5)
+    V = cpmap.direct(atoms_cuda_f32_Nx4, lat)                 # direct sum
+    ws = cpmap.bin_atoms(atoms, lat, bin_size=4.0, cutoff=12.0)
+    Vc = cpmap.cutoff(ws, len(atoms), lat, bin_size=4.0, cutoff=12.0)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Tuple
+
+from .workloads import Lattice
+
+__all__ = [
+    "Lattice", "CpmapError", "direct", "bin_atoms", "cutoff", "bin_workspace_bytes",
+    "bin_grid", "workspace_layout", "workspace_views", "neighbor_spans", "library",
+    "library_path", "header_functions", "STATUS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libcpmap.so")
+_HEADER = os.path.join(os.path.dirname(_HERE), "include", "cpmap.h")
+
+STATUS = {0: "CPMAP_OK", 1: "CPMAP_EINVAL", 2: "CPMAP_ERANGE", 3: "CPMAP_ENOSPC",
+          4: "CPMAP_EGEOM", 5: "CPMAP_EHIP"}
+
+
+class CpmapError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({msg})")
+        self.status = status
+
+
+_lib = None
+
+_i64, _i32, _f32, _vp, _sz = (ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p,
+                              ctypes.c_size_t)
+_LAT = [_i32, _i32, _i32, _f32, _f32, _f32, _f32]
+
+_SIGNATURES = {
+    "cpmap_version": (_i32, []),
+    "cpmap_status_str": (ctypes.c_char_p, [_i32]),
+    "cpmap_direct": (_i32, [_vp, _i64, *_LAT, _vp, _vp]),
+    "cpmap_bin_workspace_bytes": (_sz, [_i64, *_LAT, _f32, _f32]),
+    "cpmap_bin_grid": (_i32, [*_LAT, _f32, _f32, ctypes.POINTER(_i32)]),
+    "cpmap_bin_atoms": (_i32, [_vp, _i64, *_LAT, _f32, _f32, _vp, _sz, _vp]),
+    "cpmap_workspace_layout": (_i32, [_i64, *_LAT, _f32, _f32, ctypes.POINTER(_i64),
+                                      ctypes.POINTER(_i64)]),
+    "cpmap_cutoff": (_i32, [_vp, _sz, _i64, *_LAT, _f32, _f32, _vp, _vp]),
+    "cpmap_neighbor_spans": (_i64, [*_LAT, _f32, _f32, _i32, _i32, _i32, ctypes.POINTER(_i32),
+                                    _i64]),
+}
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def library():
+    """The loaded libcpmap.so (ctypes), with argument types set.  Raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"libcpmap.so not found at {_LIB_PATH}; build it with "
+            "`python -c 'import __graft_entry__ as g; g.build()'` "
+            "or `python direct_coulomb_potential_amd/build.py`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def header_functions():
+    """Names of the functions include/cpmap.h declares."""
+    with open(_HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cpmap_[a-z_]+)\s*\(", text)))
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        msg = library().cpmap_status_str(status).decode()
+        raise CpmapError(fn, status, msg)
+
+
+def _lat_args(lat: Lattice):
+    return [int(lat.nx), int(lat.ny), int(lat.nz), float(lat.spacing), float(lat.origin[0]),
+            float(lat.origin[1]), float(lat.origin[2])]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(device) -> int:
+    torch = _torch()
+    return int(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_atoms(atoms):
+    torch = _torch()
+    if not isinstance(atoms, torch.Tensor):
+        raise TypeError("atoms must be a torch.Tensor")
+    if atoms.dtype != torch.float32 or atoms.dim() != 2 or atoms.shape[1] != 4:
+        raise ValueError("atoms must be float32 with shape (N, 4): x, y, z, q")
+    if not atoms.is_cuda:
+        raise ValueError("atoms must be on a GPU device")
+    if not atoms.is_contiguous():
+        raise ValueError("atoms must be contiguous")
+
+
+def _out(lat: Lattice, device, out):
+    torch = _torch()
+    shape = (lat.nz, lat.ny, lat.nx)
+    if out is None:
+        return torch.empty(shape, dtype=torch.float32, device=device)
+    if out.dtype != torch.float32 or not out.is_cuda or not out.is_contiguous() \
+            or out.numel() != lat.n_points:
+        raise ValueError("out must be a contiguous float32 GPU tensor with nx*ny*nz elements")
+    return out
+
+
+def direct(atoms, lat: Lattice, out=None):
+    """Direct Coulomb sum at every node; returns V with shape (nz, ny, nx) (x fastest)."""
+    _check_atoms(atoms)
+    V = _out(lat, atoms.device, out)
+    st = library().cpmap_direct(atoms.data_ptr() if atoms.numel() else None, atoms.shape[0],
+                                *_lat_args(lat), V.data_ptr() if V.numel() else None,
+                                _stream_ptr(atoms.device))
+    _check("cpmap_direct", st)
+    return V
+
+
+def bin_workspace_bytes(n_atoms: int, lat: Lattice, bin_size: float, cutoff: float) -> int:
+    n = library().cpmap_bin_workspace_bytes(int(n_atoms), *_lat_args(lat), float(bin_size),
+                                            float(cutoff))
+    if n == 0:
+        raise CpmapError("cpmap_bin_workspace_bytes", 1, "invalid geometry")
+    return int(n)
+
+
+def bin_grid(lat: Lattice, bin_size: float, cutoff: float) -> Tuple[int, int, int]:
+    dims = (_i32 * 3)()
+    _check("cpmap_bin_grid", library().cpmap_bin_grid(*_lat_args(lat), float(bin_size),
+                                                       float(cutoff), dims))
+    return (dims[0], dims[1], dims[2])
+
+
+def workspace_layout(n_atoms: int, lat: Lattice, bin_size: float, cutoff: float):
+    a, b = _i64(), _i64()
+    _check("cpmap_workspace_layout",
+           library().cpmap_workspace_layout(int(n_atoms), *_lat_args(lat), float(bin_size),
+                                            float(cutoff), ctypes.byref(a), ctypes.byref(b)))
+    return int(a.value), int(b.value)
+
+
+def bin_atoms(atoms, lat: Lattice, bin_size: float, cutoff: float, workspace=None):
+    """Bin atoms on the GPU into a workspace (uint8 tensor) and return it."""
+    torch = _torch()
+    _check_atoms(atoms)
+    need = bin_workspace_bytes(atoms.shape[0], lat, bin_size, cutoff)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=atoms.device)
+    if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 GPU tensor")
+    st = library().cpmap_bin_atoms(atoms.data_ptr() if atoms.numel() else None, atoms.shape[0],
+                                   *_lat_args(lat), float(bin_size), float(cutoff),
+                                   workspace.data_ptr(), workspace.numel(),
+                                   _stream_ptr(atoms.device))
+    _check("cpmap_bin_atoms", st)
+    return workspace
+
+
+def workspace_views(workspace, n_atoms: int, lat: Lattice, bin_size: float, cutoff: float):
+    """(bin_start int32[nbins+1], sorted float32[n_atoms, 4]) views into a workspace."""
+    bs_off, srt_off = workspace_layout(n_atoms, lat, bin_size, cutoff)
+    bx, by, bz = bin_grid(lat, bin_size, cutoff)
+    nb = bx * by * bz
+    torch = _torch()
+    starts = workspace[bs_off:bs_off + 4 * (nb + 1)].view(torch.int32)
+    srt = workspace[srt_off:srt_off + 16 * n_atoms].view(torch.float32).view(n_atoms, 4)
+    return starts, srt
+
+
+def cutoff(workspace, n_atoms: int, lat: Lattice, bin_size: float, cutoff: float, out=None):
+    """Smoothed short-range potential with cutoff binning; returns V (nz, ny, nx)."""
+    V = _out(lat, workspace.device, out)
+    st = library().cpmap_cutoff(workspace.data_ptr(), workspace.numel(), int(n_atoms),
+                                *_lat_args(lat), float(bin_size), float(cutoff), V.data_ptr(),
+                                _stream_ptr(workspace.device))
+    _check("cpmap_cutoff", st)
+    return V
+
+
+def neighbor_spans(lat: Lattice, bin_size: float, cutoff: float, tile: Tuple[int, int, int],
+                   max_spans: int = 4096):
+    """x-runs of bins (cy, cz, cx_first, cx_last) the cutoff kernel walks for one tile."""
+    buf = (_i32 * (4 * max_spans))()
+    n = library().cpmap_neighbor_spans(*_lat_args(lat), float(bin_size), float(cutoff),
+                                       int(tile[0]), int(tile[1]), int(tile[2]), buf, max_spans)
+    if n < 0:
+        raise CpmapError("cpmap_neighbor_spans", 1, "invalid arguments")
+    if n > max_spans:
+        return neighbor_spans(lat, bin_size, cutoff, tile, int(n))
+    return [tuple(buf[4 * i:4 * i + 4]) for i in range(n)]

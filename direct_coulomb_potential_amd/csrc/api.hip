@@ -1,0 +1,291 @@
+// C ABI of libcpmap: argument checks on the host, then stream-ordered launches.
+// Every check happens before the first HIP call, so a rejected call enqueues
+// nothing and touches no device state.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <unordered_map>
+
+#include "cpmap_internal.h"
+
+namespace cpmap {
+
+namespace {
+
+bool finite_pos(float v) { return std::isfinite(v) && v > 0.0f; }
+
+cpmap_status check_lattice(int32_t nx, int32_t ny, int32_t nz, float h, float ox, float oy,
+                           float oz)
+{
+    if (nx < 0 || ny < 0 || nz < 0)
+        return CPMAP_EINVAL;
+    if (!finite_pos(h) || !std::isfinite(ox) || !std::isfinite(oy) || !std::isfinite(oz))
+        return CPMAP_EINVAL;
+    if (nx > CPMAP_MAX_DIM || ny > CPMAP_MAX_DIM || nz > CPMAP_MAX_DIM)
+        return CPMAP_ERANGE;
+    if ((int64_t)nx * ny * nz > CPMAP_MAX_POINTS)
+        return CPMAP_ERANGE;
+    return CPMAP_OK;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Host-side record of the geometry each workspace was binned for, so that
+// cpmap_cutoff can reject a workspace binned for something else without
+// reading device memory.
+struct WorkspaceKey {
+    int64_t n_atoms;
+    int32_t n[3];
+    float h, o[3], bs, rc;
+    bool operator==(const WorkspaceKey &k) const { return std::memcmp(this, &k, sizeof k) == 0; }
+};
+
+std::mutex g_mu;
+std::unordered_map<const void *, WorkspaceKey> g_binned;
+
+WorkspaceKey make_key(int64_t n_atoms, int32_t nx, int32_t ny, int32_t nz, float h, float ox,
+                      float oy, float oz, float bs, float rc)
+{
+    WorkspaceKey k;
+    std::memset(&k, 0, sizeof k);  // padding bytes take part in operator==
+    k.n_atoms = n_atoms;
+    k.n[0] = nx;
+    k.n[1] = ny;
+    k.n[2] = nz;
+    k.h = h;
+    k.o[0] = ox;
+    k.o[1] = oy;
+    k.o[2] = oz;
+    k.bs = bs;
+    k.rc = rc;
+    return k;
+}
+
+Lattice make_lattice(int32_t nx, int32_t ny, int32_t nz, float h, float ox, float oy, float oz)
+{
+    Lattice l;
+    l.n[0] = nx;
+    l.n[1] = ny;
+    l.n[2] = nz;
+    l.h = h;
+    l.o[0] = ox;
+    l.o[1] = oy;
+    l.o[2] = oz;
+    return l;
+}
+
+// Bin grid along one axis (the header's bin-geometry paragraph).
+cpmap_status axis_bins(int32_t n, float h, float o, float bs, int32_t halo, AxisBins *out)
+{
+    out->b0 = fmaf(-(float)halo, bs, o);
+    if (!std::isfinite(out->b0))
+        return CPMAP_ERANGE;
+    const float last = node_coord(n - 1, h, o);
+    const float t = bin_coord(last, out->b0, bs);
+    if (!(t >= 0.0f) || !(t < 1.0e8f))
+        return CPMAP_ERANGE;
+    const int64_t nb = (int64_t)std::floor(t) + 1 + halo;
+    if (nb > (1 << 24))
+        return CPMAP_ERANGE;
+    out->nb = (int32_t)nb;
+    return CPMAP_OK;
+}
+
+}  // namespace
+
+cpmap_status make_bin_geometry(int32_t nx, int32_t ny, int32_t nz, float h, float ox, float oy,
+                               float oz, float bin_size, float cutoff, BinGeometry *g)
+{
+    cpmap_status st = check_lattice(nx, ny, nz, h, ox, oy, oz);
+    if (st != CPMAP_OK)
+        return st;
+    if (nx == 0 || ny == 0 || nz == 0)
+        return CPMAP_EINVAL;
+    if (!finite_pos(bin_size) || !finite_pos(cutoff))
+        return CPMAP_EINVAL;
+    const float ratio = std::ceil(cutoff / bin_size);
+    if (!(ratio <= 4096.0f))
+        return CPMAP_ERANGE;
+    g->halo = (int32_t)ratio;
+    g->bin_size = bin_size;
+    g->cutoff = cutoff;
+    const int32_t n[3] = {nx, ny, nz};
+    const float o[3] = {ox, oy, oz};
+    for (int a = 0; a < 3; ++a) {
+        st = axis_bins(n[a], h, o[a], bin_size, g->halo, &g->ax[a]);
+        if (st != CPMAP_OK)
+            return st;
+    }
+    if (g->nbins() >= (int64_t)INT32_MAX)
+        return CPMAP_ERANGE;
+    return CPMAP_OK;
+}
+
+}  // namespace cpmap
+
+using namespace cpmap;
+
+extern "C" {
+
+int32_t cpmap_version(void) { return (0 << 16) | (1 << 8) | 0; }
+
+const char *cpmap_status_str(int32_t status)
+{
+    switch (status) {
+    case CPMAP_OK:
+        return "ok";
+    case CPMAP_EINVAL:
+        return "invalid argument";
+    case CPMAP_ERANGE:
+        return "size or index out of range";
+    case CPMAP_ENOSPC:
+        return "workspace too small";
+    case CPMAP_EGEOM:
+        return "workspace not binned for these arguments";
+    case CPMAP_EHIP:
+        return "HIP launch error";
+    default:
+        return "unknown status";
+    }
+}
+
+cpmap_status cpmap_direct(const float *atoms, int64_t n_atoms, int32_t nx, int32_t ny,
+                          int32_t nz, float spacing, float ox, float oy, float oz, float *V,
+                          void *stream)
+{
+    if (n_atoms < 0)
+        return CPMAP_EINVAL;
+    if (n_atoms > CPMAP_MAX_ATOMS)
+        return CPMAP_ERANGE;
+    cpmap_status st = check_lattice(nx, ny, nz, spacing, ox, oy, oz);
+    if (st != CPMAP_OK)
+        return st;
+    const Lattice lat = make_lattice(nx, ny, nz, spacing, ox, oy, oz);
+    if (lat.points() == 0)
+        return CPMAP_OK;
+    if (V == nullptr || (n_atoms > 0 && atoms == nullptr))
+        return CPMAP_EINVAL;
+    if (!aligned(V, 4) || (atoms && !aligned(atoms, 16)))
+        return CPMAP_EINVAL;
+    hipError_t e = launch_direct(reinterpret_cast<const float4 *>(atoms), n_atoms, lat, V,
+                                 static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? CPMAP_OK : CPMAP_EHIP;
+}
+
+cpmap_status cpmap_bin_grid(int32_t nx, int32_t ny, int32_t nz, float spacing, float ox, float oy,
+                            float oz, float bin_size, float cutoff, int32_t *dims_out)
+{
+    if (dims_out == nullptr)
+        return CPMAP_EINVAL;
+    BinGeometry g;
+    cpmap_status st = make_bin_geometry(nx, ny, nz, spacing, ox, oy, oz, bin_size, cutoff, &g);
+    if (st != CPMAP_OK)
+        return st;
+    for (int a = 0; a < 3; ++a)
+        dims_out[a] = g.ax[a].nb;
+    return CPMAP_OK;
+}
+
+size_t cpmap_bin_workspace_bytes(int64_t n_atoms, int32_t nx, int32_t ny, int32_t nz,
+                                 float spacing, float ox, float oy, float oz, float bin_size,
+                                 float cutoff)
+{
+    if (n_atoms < 0 || n_atoms > CPMAP_MAX_ATOMS)
+        return 0;
+    BinGeometry g;
+    if (make_bin_geometry(nx, ny, nz, spacing, ox, oy, oz, bin_size, cutoff, &g) != CPMAP_OK)
+        return 0;
+    return bin_layout(n_atoms, g).total;
+}
+
+cpmap_status cpmap_workspace_layout(int64_t n_atoms, int32_t nx, int32_t ny, int32_t nz,
+                                    float spacing, float ox, float oy, float oz, float bin_size,
+                                    float cutoff, int64_t *bin_start_offset,
+                                    int64_t *sorted_offset)
+{
+    if (bin_start_offset)
+        *bin_start_offset = -1;
+    if (sorted_offset)
+        *sorted_offset = -1;
+    if (bin_start_offset == nullptr || sorted_offset == nullptr || n_atoms < 0)
+        return CPMAP_EINVAL;
+    if (n_atoms > CPMAP_MAX_ATOMS)
+        return CPMAP_ERANGE;
+    BinGeometry g;
+    cpmap_status st = make_bin_geometry(nx, ny, nz, spacing, ox, oy, oz, bin_size, cutoff, &g);
+    if (st != CPMAP_OK)
+        return st;
+    const BinLayout L = bin_layout(n_atoms, g);
+    *bin_start_offset = (int64_t)L.bin_start;
+    *sorted_offset = (int64_t)L.sorted;
+    return CPMAP_OK;
+}
+
+cpmap_status cpmap_bin_atoms(const float *atoms, int64_t n_atoms, int32_t nx, int32_t ny,
+                             int32_t nz, float spacing, float ox, float oy, float oz,
+                             float bin_size, float cutoff, void *workspace,
+                             size_t workspace_bytes, void *stream)
+{
+    if (n_atoms < 0)
+        return CPMAP_EINVAL;
+    if (n_atoms > CPMAP_MAX_ATOMS)
+        return CPMAP_ERANGE;
+    BinGeometry g;
+    cpmap_status st = make_bin_geometry(nx, ny, nz, spacing, ox, oy, oz, bin_size, cutoff, &g);
+    if (st != CPMAP_OK)
+        return st;
+    if (workspace == nullptr || (n_atoms > 0 && atoms == nullptr))
+        return CPMAP_EINVAL;
+    if (!aligned(workspace, 256) || (atoms && !aligned(atoms, 16)))
+        return CPMAP_EINVAL;
+    const BinLayout L = bin_layout(n_atoms, g);
+    if (workspace_bytes < L.total)
+        return CPMAP_ENOSPC;
+    const Lattice lat = make_lattice(nx, ny, nz, spacing, ox, oy, oz);
+    {
+        std::lock_guard<std::mutex> lock(g_mu);
+        g_binned.erase(workspace);
+    }
+    hipError_t e = launch_bin_atoms(reinterpret_cast<const float4 *>(atoms), n_atoms, lat, g, L,
+                                    workspace, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return CPMAP_EHIP;
+    std::lock_guard<std::mutex> lock(g_mu);
+    g_binned[workspace] = make_key(n_atoms, nx, ny, nz, spacing, ox, oy, oz, bin_size, cutoff);
+    return CPMAP_OK;
+}
+
+cpmap_status cpmap_cutoff(const void *workspace, size_t workspace_bytes, int64_t n_atoms,
+                          int32_t nx, int32_t ny, int32_t nz, float spacing, float ox, float oy,
+                          float oz, float bin_size, float cutoff, float *V, void *stream)
+{
+    if (n_atoms < 0)
+        return CPMAP_EINVAL;
+    if (n_atoms > CPMAP_MAX_ATOMS)
+        return CPMAP_ERANGE;
+    BinGeometry g;
+    cpmap_status st = make_bin_geometry(nx, ny, nz, spacing, ox, oy, oz, bin_size, cutoff, &g);
+    if (st != CPMAP_OK)
+        return st;
+    if (workspace == nullptr || V == nullptr)
+        return CPMAP_EINVAL;
+    if (!aligned(workspace, 256) || !aligned(V, 4))
+        return CPMAP_EINVAL;
+    const BinLayout L = bin_layout(n_atoms, g);
+    if (workspace_bytes < L.total)
+        return CPMAP_ENOSPC;
+    {
+        std::lock_guard<std::mutex> lock(g_mu);
+        auto it = g_binned.find(workspace);
+        if (it == g_binned.end() ||
+            !(it->second == make_key(n_atoms, nx, ny, nz, spacing, ox, oy, oz, bin_size, cutoff)))
+            return CPMAP_EGEOM;
+    }
+    const Lattice lat = make_lattice(nx, ny, nz, spacing, ox, oy, oz);
+    hipError_t e = launch_cutoff(workspace, L, n_atoms, lat, g, V,
+                                 static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? CPMAP_OK : CPMAP_EHIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,84 @@
+// Internal declarations shared by the cpmap host code and kernels (not the oracle).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/cpmap.h"
+
+namespace cpmap {
+
+// Node coordinate along one axis: one fp32 rounding of origin + i*h (the
+// header's lattice convention).  Same expression on host and device.
+__host__ __device__ inline float node_coord(int64_t i, float h, float origin)
+{
+    return fmaf(static_cast<float>(i), h, origin);
+}
+
+// Bin grid of one axis (the header's bin-geometry paragraph).
+struct AxisBins {
+    float b0;    // bin-grid origin
+    int32_t nb;  // bins along the axis
+};
+
+struct BinGeometry {
+    AxisBins ax[3];
+    int32_t halo;
+    float bin_size;
+    float cutoff;
+    int64_t nbins() const { return (int64_t)ax[0].nb * ax[1].nb * ax[2].nb; }
+};
+
+// Bin coordinate of a position: fp32 subtract, then fp32 divide (both
+// correctly rounded; hipcc keeps the IEEE divide by default).
+__host__ __device__ inline float bin_coord(float p, float b0, float bs)
+{
+    const float d = p - b0;
+    return d / bs;
+}
+
+// Fills g; returns CPMAP_OK, CPMAP_EINVAL or CPMAP_ERANGE.
+cpmap_status make_bin_geometry(int32_t nx, int32_t ny, int32_t nz, float h,
+                               float ox, float oy, float oz, float bin_size, float cutoff,
+                               BinGeometry *g);
+
+// ---- launchers (host) -------------------------------------------------------
+
+struct Lattice {
+    int32_t n[3];
+    float h;
+    float o[3];
+    int64_t points() const { return (int64_t)n[0] * n[1] * n[2]; }
+};
+
+hipError_t launch_direct(const float4 *atoms, int64_t n_atoms, const Lattice &lat, float *V,
+                         hipStream_t stream);
+
+// Workspace layout of the binned atoms.
+struct BinLayout {
+    size_t header;      // geometry header (bytes)
+    size_t bin_start;   // offset of int32[nbins + 1]
+    size_t sorted;      // offset of float4[n_atoms]
+    size_t keys[2];     // int32[n_pad] radix-sort key ping-pong
+    size_t vals[2];     // int32[n_pad] radix-sort value ping-pong
+    size_t hist;        // int32[256 * n_tiles] digit counts per tile
+    size_t total;
+    int64_t n_tiles;    // radix-sort tiles
+    int32_t passes;     // radix passes (8 bits each)
+};
+
+BinLayout bin_layout(int64_t n_atoms, const BinGeometry &g);
+
+hipError_t launch_bin_atoms(const float4 *atoms, int64_t n_atoms, const Lattice &lat,
+                            const BinGeometry &g, const BinLayout &L, void *workspace,
+                            hipStream_t stream);
+
+hipError_t launch_cutoff(const void *workspace, const BinLayout &L, int64_t n_atoms,
+                         const Lattice &lat, const BinGeometry &g, float *V, hipStream_t stream);
+
+// Neighbourhood of one 8x8x8 tile as x-runs of bins; host and device.
+constexpr int kTile = 8;
+
+}  // namespace cpmap

@@ -1,0 +1,204 @@
+/*
+ * cpmap.h -- electrostatic potential maps on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libcpmap.so.  Plain C: no HIP, torch or C++ types.  All calls are
+ * host functions.  Unless a comment says "host", a pointer argument is a
+ * device pointer (hipMalloc'd memory, or any memory the GPU can address).
+ *
+ * Common conventions
+ *   - Atoms are n_atoms rows of 4 floats (x, y, z, q): positions in Angstrom,
+ *     charges in units of e, 16-byte aligned, one float4 per atom.
+ *   - The lattice has nx*ny*nz nodes; node (i,j,k) sits at
+ *       (fl(ox + i*spacing), fl(oy + j*spacing), fl(oz + k*spacing))
+ *     where fl() is one rounding to fp32 (the notes' gather listing puts node
+ *     (gx,gy,gz) at (gx,gy,gz)*h with a zero origin; the origin is the
+ *     generalisation).  V holds one fp32 per node, x-fastest:
+ *       V[(k*ny + j)*nx + i]
+ *     (the notes' section 18.4 on lattice index order).
+ *   - Potentials are in e/Angstrom; no Coulomb constant is applied.
+ *   - No call allocates or frees memory, synchronises, or prints.  Every GPU
+ *     call is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     returns before the work finishes.  Execution faults surface at the
+ *     caller's next synchronisation of that stream.
+ *   - Arguments are checked on the host before any HIP call; a failed check
+ *     returns a status and enqueues nothing.  Device data is not inspected:
+ *     an atom placed exactly on a node gives an infinite potential there, and
+ *     non-finite atom data propagates into V.
+ *   - Results are deterministic: the same inputs give bit-identical outputs.
+ */
+#ifndef CPMAP_H
+#define CPMAP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum cpmap_status {
+    CPMAP_OK = 0,
+    CPMAP_EINVAL = 1, /* null pointer, negative count, dimension < 0, spacing /
+                         bin size / cutoff not finite or <= 0, misaligned ptr */
+    CPMAP_ERANGE = 2, /* a count or index does not fit the library's limits */
+    CPMAP_ENOSPC = 3, /* workspace smaller than cpmap_bin_workspace_bytes() */
+    CPMAP_EGEOM = 4,  /* workspace was binned for another geometry or atom
+                         count, or was never binned */
+    CPMAP_EHIP = 5    /* the HIP runtime reported an error at launch */
+} cpmap_status;
+
+/* Library version, (major << 16) | (minor << 8) | patch.  Host. */
+int32_t cpmap_version(void);
+
+/* Static, human-readable name of a status code.  Host; never NULL. */
+const char *cpmap_status_str(int32_t status);
+
+/* Limits: n_atoms <= CPMAP_MAX_ATOMS; each lattice dimension <= CPMAP_MAX_DIM
+ * (so that every node index is exact in fp32); nx*ny*nz <= CPMAP_MAX_POINTS. */
+#define CPMAP_MAX_ATOMS 2147483647LL
+#define CPMAP_MAX_DIM 16777216
+#define CPMAP_MAX_POINTS 68719476736LL
+
+/*
+ * cpmap_direct -- direct Coulomb summation over every atom.
+ *
+ * Computes V(g) = sum_a q_a / |g - a| at every lattice node g (the notes'
+ * section 18.1 formula; section 18.2's gather mapping: each output node is
+ * written once, by one GPU lane, with no atomics).  V is OVERWRITTEN with the
+ * full sum (no accumulation into previous contents); n_atoms = 0 writes zeros.
+ * A lattice with a zero dimension is a no-op (V may then be NULL).
+ *
+ *   atoms       device, n_atoms x float4 (x, y, z, q); read only
+ *   n_atoms     0 <= n_atoms <= CPMAP_MAX_ATOMS
+ *   nx, ny, nz  lattice dimensions, 0 <= n <= CPMAP_MAX_DIM
+ *   spacing     lattice spacing h (finite, > 0)
+ *   ox, oy, oz  position of node (0,0,0) (finite)
+ *   V           device, nx*ny*nz floats, written
+ *   stream      hipStream_t or NULL
+ * Ownership: the caller owns atoms and V; both must stay valid until the
+ * enqueued work completes.  Accuracy: fp32 with the hardware reciprocal
+ * square root; |V - V_exact| <= 1e-5 * sum_a |q_a| / r at every node.
+ */
+cpmap_status cpmap_direct(const float *atoms, int64_t n_atoms,
+                          int32_t nx, int32_t ny, int32_t nz, float spacing,
+                          float ox, float oy, float oz,
+                          float *V, void *stream);
+
+/*
+ * Bin geometry (shared by the three cutoff calls below).  With bin size bs
+ * and cutoff rc: halo H = ceil(rc/bs) bins on every side of the lattice; bin
+ * grid origin b0 = fl(o - H*bs) per axis; nb per axis = floor(t_last) + 1 + H
+ * with t_last the bin coordinate of the axis' last node.  An atom's bin
+ * coordinate per axis is t = fl(fl(p - b0) / bs) in fp32; the atom is kept iff
+ * 0 <= t < nb on every axis and then sits in bin floor(t) (the binning
+ * lecture's pseudo-code slide: bin index = position / BIN_SIZE).  Atoms
+ * outside the halo are at least rc from every node and are dropped.  Bins
+ * are numbered x-fastest: (cz*nby + cy)*nbx + cx.
+ */
+
+/*
+ * cpmap_bin_workspace_bytes -- size of the workspace that cpmap_bin_atoms
+ * fills and cpmap_cutoff reads, for this atom count and geometry.  Host only,
+ * no HIP call.  Returns 0 when the arguments are invalid or too large.
+ */
+size_t cpmap_bin_workspace_bytes(int64_t n_atoms,
+                                 int32_t nx, int32_t ny, int32_t nz, float spacing,
+                                 float ox, float oy, float oz,
+                                 float bin_size, float cutoff);
+
+/*
+ * cpmap_bin_grid -- the bin-grid dimensions for a geometry.  Host only, no
+ * HIP call.  dims_out (host, 3 int32) receives bins per axis; returns
+ * CPMAP_OK or CPMAP_EINVAL / CPMAP_ERANGE.
+ */
+cpmap_status cpmap_bin_grid(int32_t nx, int32_t ny, int32_t nz, float spacing,
+                            float ox, float oy, float oz,
+                            float bin_size, float cutoff, int32_t *dims_out);
+
+/*
+ * cpmap_bin_atoms -- spatial binning of atoms (the binning lecture's
+ * pseudo-code slide, step 1; the notes' section 18.5 BinTable: bins
+ * flattened into one atom array with a start offset per bin).
+ *
+ * Sorts the atoms stably by bin on the GPU (input order kept inside a bin)
+ * and writes, inside `workspace`:
+ *   bin_start  (nbins + 1) int32: bin b holds sorted[bin_start[b] ..
+ *              bin_start[b+1]); bin_start[nbins] = kept atoms
+ *   sorted     float4 atoms in bin order
+ * (offsets of both: cpmap_workspace_layout).  Also records, on the host, the
+ * geometry the workspace was binned for, so that cpmap_cutoff can check it.
+ *
+ *   atoms, n_atoms, nx..oz   as in cpmap_direct
+ *   bin_size, cutoff         finite, > 0 (Angstrom)
+ *   workspace                device, >= cpmap_bin_workspace_bytes(...) bytes,
+ *                            256-byte aligned; overwritten
+ *   workspace_bytes          its size
+ * Ownership: caller owns everything; the workspace must stay valid and
+ * untouched until cpmap_cutoff's work on it completes.
+ */
+cpmap_status cpmap_bin_atoms(const float *atoms, int64_t n_atoms,
+                             int32_t nx, int32_t ny, int32_t nz, float spacing,
+                             float ox, float oy, float oz,
+                             float bin_size, float cutoff,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * cpmap_workspace_layout -- byte offsets of bin_start and sorted inside a
+ * workspace of this geometry (host only, no HIP call); -1 offsets on error.
+ */
+cpmap_status cpmap_workspace_layout(int64_t n_atoms,
+                                    int32_t nx, int32_t ny, int32_t nz, float spacing,
+                                    float ox, float oy, float oz,
+                                    float bin_size, float cutoff,
+                                    int64_t *bin_start_offset, int64_t *sorted_offset);
+
+/*
+ * cpmap_cutoff -- smoothed short-range potential with cutoff binning.
+ *
+ * For every node g: V(g) = sum over atoms with |g - a|^2 < rc^2 of
+ *   q_a * (1/r - (GC0 + r^2 (GC1 + r^2 GC2))),
+ *   GC0 = 15/(8 rc), GC1 = -5/(4 rc^3), GC2 = 3/(8 rc^5)
+ * (the binning lecture's large-bin kernel slide gives the term's form; the
+ * constants make it vanish with its first two derivatives at rc).  Each
+ * workgroup owns an 8x8x8 tile of nodes, walks the neighbourhood of bins
+ * whose box lies within rc of the tile (the lecture's neighbourhood offset
+ * list), stages those bins' atoms in LDS and evaluates the term for each of
+ * its nodes (the lecture's small-bin design).  V is OVERWRITTEN.
+ *
+ *   workspace, workspace_bytes   filled by cpmap_bin_atoms for the same
+ *                                n_atoms and geometry; read only
+ *   n_atoms, nx..cutoff          the values given to cpmap_bin_atoms
+ *   V                            device, nx*ny*nz floats, written
+ * Returns CPMAP_EGEOM if the workspace was not binned for these arguments.
+ * Accuracy: |V - V_exact| <= 1e-5 * sum_{r < rc} |q| / r at every node.
+ */
+cpmap_status cpmap_cutoff(const void *workspace, size_t workspace_bytes, int64_t n_atoms,
+                          int32_t nx, int32_t ny, int32_t nz, float spacing,
+                          float ox, float oy, float oz,
+                          float bin_size, float cutoff,
+                          float *V, void *stream);
+
+/*
+ * cpmap_neighbor_spans -- the neighbourhood the cutoff kernel walks for one
+ * tile, for inspection and tests.  Host only, no HIP call.
+ *
+ * The tile with tile coordinates (tx, ty, tz) holds nodes
+ * [8tx, 8tx+8) x [8ty, 8ty+8) x [8tz, 8tz+8) clipped to the lattice.  A bin is
+ * in its neighbourhood iff the distance between the tile's node bounding box
+ * and the bin's box is < cutoff.  Such bins form runs along x; each run is
+ * reported as (cy, cz, cx_first, cx_last) in spans_out (host, 4 int32 per
+ * span, capacity max_spans).  Returns the number of spans (possibly larger
+ * than max_spans, in which case only max_spans were written), or -1 on
+ * invalid arguments.
+ */
+int64_t cpmap_neighbor_spans(int32_t nx, int32_t ny, int32_t nz, float spacing,
+                             float ox, float oy, float oz,
+                             float bin_size, float cutoff,
+                             int32_t tx, int32_t ty, int32_t tz,
+                             int32_t *spans_out, int64_t max_spans);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CPMAP_H */

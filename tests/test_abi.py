@@ -1,0 +1,121 @@
+"""The C ABI without a GPU: the library loads, exports every function the header
+declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import math
+import subprocess
+
+import pytest
+
+import direct_coulomb_potential_amd as cpmap
+from direct_coulomb_potential_amd import Lattice
+
+OK, EINVAL, ERANGE, ENOSPC, EGEOM = 0, 1, 2, 3, 4
+LAT = [8, 8, 8, 0.5, 0.0, 0.0, 0.0]
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its host checks
+
+
+def test_header_functions_are_exported():
+    names = cpmap.header_functions()
+    assert {"cpmap_direct", "cpmap_bin_atoms", "cpmap_cutoff"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", cpmap.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    lib = cpmap.library()
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def test_version_and_status_strings():
+    lib = cpmap.library()
+    assert lib.cpmap_version() >= (0 << 16) | (1 << 8)
+    for s in range(6):
+        assert lib.cpmap_status_str(s)
+    assert lib.cpmap_status_str(99) == b"unknown status"
+
+
+@pytest.mark.parametrize("args,want", [
+    (dict(n=-1), EINVAL),
+    (dict(n=2**31), ERANGE),
+    (dict(nx=-1), EINVAL),
+    (dict(nx=2**24 + 1), ERANGE),
+    (dict(nx=2**24, ny=2**24, nz=2), ERANGE),
+    (dict(h=0.0), EINVAL),
+    (dict(h=-0.5), EINVAL),
+    (dict(h=math.nan), EINVAL),
+    (dict(h=math.inf), EINVAL),
+    (dict(ox=math.nan), EINVAL),
+    (dict(oz=math.inf), EINVAL),
+    (dict(V=None), EINVAL),
+    (dict(atoms=None), EINVAL),
+    (dict(atoms=ctypes.c_void_p(0x1004)), EINVAL),  # not 16-byte aligned
+    (dict(V=ctypes.c_void_p(0x1002)), EINVAL),      # not 4-byte aligned
+    (dict(nx=0, V=None), OK),                       # empty lattice: no-op, no HIP call
+    (dict(ny=0, atoms=None, V=None), OK),
+])
+def test_direct_argument_checks(args, want):
+    a = dict(atoms=FAKE, n=10, nx=8, ny=8, nz=8, h=0.5, ox=0.0, oy=0.0, oz=0.0, V=FAKE)
+    a.update(args)
+    st = cpmap.library().cpmap_direct(a["atoms"], a["n"], a["nx"], a["ny"], a["nz"], a["h"],
+                                      a["ox"], a["oy"], a["oz"], a["V"], None)
+    assert st == want
+
+
+def test_bin_geometry_queries_match_the_header_rule():
+    lat = Lattice(200, 200, 200, 0.5)
+    assert cpmap.bin_grid(lat, 4.0, 12.0) == (31, 31, 31)
+    lat2 = Lattice(10, 3, 5, 0.5, (1.0, -2.0, 0.25))
+    assert cpmap.bin_grid(lat2, 1.5, 1.5) == (6, 3, 4)
+    n = cpmap.bin_workspace_bytes(100_000, lat, 4.0, 12.0)
+    bs_off, srt_off = cpmap.workspace_layout(100_000, lat, 4.0, 12.0)
+    assert bs_off % 256 == 0 and srt_off % 256 == 0
+    assert srt_off >= bs_off + 4 * (31**3 + 1)
+    assert n >= srt_off + 16 * 100_000
+
+
+@pytest.mark.parametrize("bs,rc,want", [
+    (0.0, 12.0, EINVAL), (4.0, 0.0, EINVAL), (math.nan, 12.0, EINVAL), (4.0, math.inf, EINVAL),
+    (-1.0, 12.0, EINVAL), (1e-6, 12.0, ERANGE),
+])
+def test_bin_grid_rejects_bad_bins(bs, rc, want):
+    dims = (ctypes.c_int32 * 3)()
+    assert cpmap.library().cpmap_bin_grid(*LAT, bs, rc, dims) == want
+
+
+def test_bin_and_cutoff_argument_checks():
+    lib = cpmap.library()
+    need = lib.cpmap_bin_workspace_bytes(100, *LAT, 1.0, 2.0)
+    assert need > 0
+    assert lib.cpmap_bin_workspace_bytes(-1, *LAT, 1.0, 2.0) == 0
+    assert lib.cpmap_bin_workspace_bytes(100, *LAT, 0.0, 2.0) == 0
+    ws = ctypes.c_void_p(0x10000)
+    # too small a workspace, misaligned workspace, null atoms, bad counts
+    assert lib.cpmap_bin_atoms(FAKE, 100, *LAT, 1.0, 2.0, ws, need - 1, None) == ENOSPC
+    assert lib.cpmap_bin_atoms(FAKE, 100, *LAT, 1.0, 2.0, ctypes.c_void_p(0x10010), need, None) == EINVAL
+    assert lib.cpmap_bin_atoms(None, 100, *LAT, 1.0, 2.0, ws, need, None) == EINVAL
+    assert lib.cpmap_bin_atoms(FAKE, -5, *LAT, 1.0, 2.0, ws, need, None) == EINVAL
+    assert lib.cpmap_bin_atoms(FAKE, 100, 0, 8, 8, 0.5, 0, 0, 0, 1.0, 2.0, ws, need, None) == EINVAL
+    # a workspace that was never binned is rejected by cutoff, before any HIP call
+    assert lib.cpmap_cutoff(ws, need, 100, *LAT, 1.0, 2.0, FAKE, None) == EGEOM
+    assert lib.cpmap_cutoff(ws, need - 1, 100, *LAT, 1.0, 2.0, FAKE, None) == ENOSPC
+    assert lib.cpmap_cutoff(ws, need, 100, *LAT, 1.0, 2.0, None, None) == EINVAL
+    assert lib.cpmap_cutoff(None, need, 100, *LAT, 1.0, 2.0, FAKE, None) == EINVAL
+
+
+def test_layout_query_errors():
+    lib = cpmap.library()
+    a, b = ctypes.c_int64(), ctypes.c_int64()
+    assert lib.cpmap_workspace_layout(-1, *LAT, 1.0, 2.0, ctypes.byref(a), ctypes.byref(b)) == EINVAL
+    assert a.value == -1 and b.value == -1
+    assert lib.cpmap_workspace_layout(5, *LAT, 1.0, 2.0, None, ctypes.byref(b)) == EINVAL
+
+
+def test_binding_rejects_cpu_and_wrong_dtype_tensors():
+    torch = pytest.importorskip("torch")
+    with pytest.raises(ValueError):
+        cpmap.direct(torch.zeros(4, 4), Lattice(2, 2, 2, 0.5))
+    with pytest.raises(ValueError):
+        cpmap.direct(torch.zeros(4, 3, dtype=torch.float32), Lattice(2, 2, 2, 0.5))
+    with pytest.raises(TypeError):
+        cpmap.direct([[0, 0, 0, 1]], Lattice(2, 2, 2, 0.5))

@@ -1,0 +1,141 @@
+"""GPU parity of cpmap_direct against the fp64 oracle.
+
+Bar: |V_gpu - V_oracle| <= 1e-5 * S at every checked node, S = sum_a |q_a|/r.
+Small cases are checked at every node; the 200^3 workloads on three full
+z-slices plus 10^4 seeded random nodes, in the same launch configuration the
+benchmark times (the library picks it from the lattice and atom count).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import direct_coulomb_potential_amd as cpmap
+from direct_coulomb_potential_amd import Lattice
+from direct_coulomb_potential_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the gpu tests need an MI355X")
+    return torch
+
+
+def _run_direct(torch, atoms_np, lat):
+    atoms = torch.from_numpy(np.ascontiguousarray(atoms_np, dtype=np.float32)).cuda()
+    V = cpmap.direct(atoms, lat)
+    torch.cuda.synchronize()
+    return V.cpu().numpy().reshape(-1)
+
+
+def _assert_parity(Vg, Vo, S, label):
+    err = np.abs(Vg.astype(np.float64) - Vo)
+    ratio = err / np.where(S > 0, S, 1.0)
+    worst = int(np.argmax(ratio)) if ratio.size else 0
+    assert np.all(np.isfinite(Vg)), f"{label}: non-finite output"
+    assert np.all(err <= TOL * S), (
+        f"{label}: max |err|/S = {ratio.max():.3e} at node {worst} "
+        f"(gpu {Vg[worst]!r}, oracle {Vo[worst]!r}, S {S[worst]!r})")
+    return float(ratio.max()) if ratio.size else 0.0
+
+
+CASES = [
+    # (n_atoms, dims, spacing, origin, box_lo, box_hi, seed)
+    (1, (1, 1, 1), 0.5, (0.0, 0.0, 0.0), (-2, -2, -2), (2, 2, 2), 1),
+    (3, (13, 7, 3), 0.5, (0.0, 0.0, 0.0), (0, 0, 0), (6, 3, 1), 2),
+    (63, (17, 9, 5), 0.3, (-1.0, 0.5, 2.0), (-2, 0, 1), (5, 4, 4), 3),
+    (65, (100, 1, 1), 0.5, (0.0, 0.0, 0.0), (-5, -1, -1), (55, 1, 1), 4),
+    (257, (1, 100, 3), 0.25, (3.0, -4.0, 0.0), (0, -6, -1), (6, 22, 2), 5),
+    (1000, (33, 31, 29), 0.5, (-8.0, -7.5, -7.0), (-12, -12, -12), (12, 12, 12), 6),
+    (4099, (64, 64, 16), 0.5, (0.0, 0.0, 0.0), (-10, -10, -10), (42, 42, 18), 7),
+    (70_000, (24, 20, 18), 1.0, (0.0, 0.0, 0.0), (-5, -5, -5), (30, 30, 30), 8),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"n{c[0]}_{c[1][0]}x{c[1][1]}x{c[1][2]}" for c in CASES])
+def test_direct_small_all_nodes(torch, case):
+    n, dims, h, origin, lo, hi, seed = case
+    atoms = wl.random_atoms(n, lo, hi, seed=seed)
+    lat = Lattice(*dims, h, origin)
+    print(f"[direct] n={n} dims={dims} h={h} origin={origin}", flush=True)
+    Vg = _run_direct(torch, atoms, lat)
+    Vo, S = oracle.direct(atoms, dims, h, origin, with_scale=True)
+    _assert_parity(Vg, Vo, S, f"n={n} dims={dims}")
+
+
+def test_direct_no_atoms_writes_zeros(torch):
+    lat = Lattice(9, 5, 3, 0.5)
+    out = torch.full((3, 5, 9), 7.0, device="cuda")
+    V = cpmap.direct(torch.zeros((0, 4), device="cuda"), lat, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(V == 0).item()
+
+
+def test_direct_zero_charges_and_far_atoms(torch):
+    """q = 0 atoms add exactly nothing; atoms far outside the lattice count."""
+    atoms = wl.random_atoms(300, (-50, -50, -50), (60, 60, 60), seed=9)
+    atoms[::3, 3] = 0.0
+    lat = Lattice(11, 10, 9, 0.5, (2.0, 2.0, 2.0))
+    Vg = _run_direct(torch, atoms, lat)
+    Vo, S = oracle.direct(atoms, lat.dims, lat.spacing, lat.origin, with_scale=True)
+    _assert_parity(Vg, Vo, S, "zero/far")
+    nz = atoms[atoms[:, 3] != 0]
+    Vg2 = _run_direct(torch, nz, lat)
+    Vo2 = oracle.direct(nz, lat.dims, lat.spacing, lat.origin)
+    _assert_parity(Vg2, Vo2, S, "zero charges removed")
+
+
+def test_direct_same_sign_charges_large_n(torch):
+    """All-positive charges over many atoms: the blocked fp32 sum must stay
+    inside the bound even though no cancellation hides rounding."""
+    atoms = wl.random_atoms(200_000, (0, 0, 0), (20, 20, 20), seed=10, q_lo=0.0, q_hi=1.0)
+    lat = Lattice(16, 12, 10, 1.25, (0.1, 0.2, 0.3))
+    Vg = _run_direct(torch, atoms, lat)
+    Vo, S = oracle.direct(atoms, lat.dims, lat.spacing, lat.origin, with_scale=True)
+    worst = _assert_parity(Vg, Vo, S, "same sign")
+    print(f"same-sign worst |err|/S = {worst:.3e}")
+
+
+def test_direct_is_deterministic(torch):
+    atoms = torch.from_numpy(wl.random_atoms(5000, (0, 0, 0), (10, 10, 10), seed=12)).cuda()
+    lat = Lattice(40, 30, 20, 0.25)
+    a = cpmap.direct(atoms, lat).clone()
+    b = cpmap.direct(atoms, lat)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_direct_rejects_unbinned_geometry_errors(torch):
+    atoms = torch.zeros((10, 4), device="cuda")
+    with pytest.raises(ValueError):
+        cpmap.direct(atoms, Lattice(2, 2, 2, 0.5), out=torch.zeros(7, device="cuda"))
+    with pytest.raises(cpmap.CpmapError):
+        cpmap.direct(atoms, Lattice(2, 2, 2, 0.0))
+
+
+@pytest.mark.parametrize("index", [1, 2])
+def test_direct_workload_all_nodes(torch, index):
+    w = wl.workload(index)
+    lat = w.lattice
+    print(f"[direct] workload {w.name}", flush=True)
+    Vg = _run_direct(torch, w.atoms, lat)
+    Vo, S = oracle.direct(w.atoms, lat.dims, lat.spacing, lat.origin, with_scale=True)
+    worst = _assert_parity(Vg, Vo, S, w.name)
+    print(f"{w.name}: worst |err|/S = {worst:.3e}")
+
+
+@pytest.mark.parametrize("index", [3, 4])
+def test_direct_workload_checked_nodes(torch, index):
+    w = wl.workload(index)
+    lat = w.lattice
+    print(f"[direct] workload {w.name}", flush=True)
+    Vg = _run_direct(torch, w.atoms, lat)
+    nodes = wl.checked_nodes(lat)
+    Vo, S = oracle.direct(w.atoms, lat.dims, lat.spacing, lat.origin, nodes=nodes, with_scale=True)
+    worst = _assert_parity(Vg[nodes], Vo, S, w.name)
+    print(f"{w.name}: {nodes.size} nodes, worst |err|/S = {worst:.3e}")
