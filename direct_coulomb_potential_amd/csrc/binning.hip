@@ -1,23 +1,258 @@
-// Spatial binning of atoms (placeholder launcher; the GPU sort follows).
+// Spatial binning of atoms on gfx950 (the binning lecture's pseudo-code slide,
+// step 1: bin index = position / BIN_SIZE, atoms appended to their bin; the
+// notes' section 18.5 BinTable: bins flattened into one atom array with a
+// start offset per bin).
+//
+// The lecture bins on the CPU into fixed 8-slot bins with an overflow list;
+// here the GPU builds a CSR (bin_start + atoms sorted by bin), so no bin can
+// overflow and the workspace size depends only on the atom count and the
+// geometry.  The sort is a stable LSD radix sort on the bin id (8-bit digits,
+// as many passes as the bin count needs), so atoms keep their input order
+// inside a bin and the output is bit-identical from run to run:
+//   keys      bin id per atom (nbins for dropped atoms, which sort last)
+//   per pass  tile histograms -> one exclusive scan (digit-major) -> stable
+//             scatter, ranking equal digits inside a wave with ballots
+//   starts    bin_start[b] = lower_bound(sorted keys, b)
+//   gather    sorted atoms = atoms[sorted indices]
 #include "cpmap_internal.h"
 
 namespace cpmap {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kItems = 8;                        // elements per thread per tile
+constexpr int kTileElems = kThreads * kItems;    // elements per radix tile
+constexpr int kDigits = 256;
+
+size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
+
+__global__ void k_keys(const float4 *__restrict__ atoms, int32_t n, float b0x, float b0y,
+                       float b0z, int32_t nbx, int32_t nby, int32_t nbz, float bs,
+                       int32_t nbins, int32_t *__restrict__ keys, int32_t *__restrict__ vals)
+{
+    const int32_t i = blockIdx.x * kThreads + threadIdx.x;
+    if (i >= n)
+        return;
+    const float4 a = atoms[i];
+    const float tx = bin_coord(a.x, b0x, bs);
+    const float ty = bin_coord(a.y, b0y, bs);
+    const float tz = bin_coord(a.z, b0z, bs);
+    const bool keep = tx >= 0.0f && tx < (float)nbx && ty >= 0.0f && ty < (float)nby &&
+                      tz >= 0.0f && tz < (float)nbz;
+    int32_t key = nbins;
+    if (keep) {
+        const int32_t cx = (int32_t)floorf(tx), cy = (int32_t)floorf(ty),
+                      cz = (int32_t)floorf(tz);
+        key = (cz * nby + cy) * nbx + cx;
+    }
+    keys[i] = key;
+    vals[i] = i;
+}
+
+// Digit counts of one tile, written digit-major: hist[d * n_tiles + tile].
+__global__ __launch_bounds__(kThreads) void k_hist(const int32_t *__restrict__ keys, int32_t n,
+                                                   int shift, int32_t n_tiles,
+                                                   int32_t *__restrict__ hist)
+{
+    __shared__ int32_t cnt[kDigits];
+    cnt[threadIdx.x] = 0;
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x * kTileElems;
+#pragma unroll
+    for (int it = 0; it < kItems; ++it) {
+        const int64_t e = base + it * kThreads + threadIdx.x;
+        if (e < n)
+            atomicAdd(&cnt[(keys[e] >> shift) & 0xff], 1);
+    }
+    __syncthreads();
+    hist[(int64_t)threadIdx.x * n_tiles + blockIdx.x] = cnt[threadIdx.x];
+}
+
+// Exclusive scan of m int32 in place, one workgroup of 1024 threads: each
+// thread scans a contiguous segment, the segment sums are scanned in LDS.
+__global__ __launch_bounds__(1024) void k_scan(int32_t *__restrict__ data, int64_t m)
+{
+    __shared__ int32_t part[1024];
+    const int t = threadIdx.x;
+    const int64_t seg = (m + 1023) / 1024;
+    const int64_t lo = t * seg < m ? t * seg : m;
+    const int64_t hi = lo + seg < m ? lo + seg : m;
+    int32_t s = 0;
+    for (int64_t i = lo; i < hi; ++i)
+        s += data[i];
+    part[t] = s;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        const int32_t v = t >= off ? part[t - off] : 0;
+        __syncthreads();
+        part[t] += v;
+        __syncthreads();
+    }
+    int32_t run = part[t] - s;  // exclusive prefix of this segment
+    for (int64_t i = lo; i < hi; ++i) {
+        const int32_t v = data[i];
+        data[i] = run;
+        run += v;
+    }
+}
+
+// Stable scatter of one tile.  The tile is walked in kItems sub-tiles of 256
+// consecutive elements (element base + it*256 + thread), so input order is
+// (sub-tile, wave, lane).  Inside a wave, lanes with the same digit are found
+// with 8 ballots; across waves and sub-tiles, per-digit counters in LDS give
+// the running offsets.
+__global__ __launch_bounds__(kThreads) void k_scatter(
+    const int32_t *__restrict__ keys_in, const int32_t *__restrict__ vals_in, int32_t n,
+    int shift, int32_t n_tiles, const int32_t *__restrict__ offsets,
+    int32_t *__restrict__ keys_out, int32_t *__restrict__ vals_out)
+{
+    constexpr int kWaves = kThreads / 64;
+    __shared__ int32_t run[kDigits];             // elements of each digit placed so far
+    __shared__ int32_t wave_cnt[kWaves][kDigits];
+    const int t = threadIdx.x;
+    const int wave = t / 64;
+    const int lane = t % 64;
+    run[t] = offsets[(int64_t)t * n_tiles + blockIdx.x];
+    for (int w = 0; w < kWaves; ++w)
+        wave_cnt[w][t] = 0;
+    __syncthreads();
+    const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    const int64_t base = (int64_t)blockIdx.x * kTileElems;
+    for (int it = 0; it < kItems; ++it) {
+        const int64_t e = base + it * kThreads + t;
+        const bool valid = e < n;
+        const int32_t key = valid ? keys_in[e] : 0;
+        const int32_t val = valid ? vals_in[e] : 0;
+        const int d = valid ? (key >> shift) & 0xff : kDigits;  // invalid lanes: own class
+        // lanes of this wave holding the same digit (invalid lanes match none)
+        uint64_t same = __ballot(valid);
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const bool bit = (d >> b) & 1;
+            const uint64_t vote = __ballot(bit);
+            same &= bit ? vote : ~vote;
+        }
+        if (!valid)
+            same = 0;
+        const int rank = __popcll(same & lt_mask);
+        if (valid && rank == 0)
+            wave_cnt[wave][d] = __popcll(same);
+        __syncthreads();
+        if (valid) {
+            int32_t pos = run[d] + rank;
+            for (int w = 0; w < wave; ++w)
+                pos += wave_cnt[w][d];
+            keys_out[pos] = key;
+            vals_out[pos] = val;
+        }
+        __syncthreads();
+        int32_t added = 0;
+        for (int w = 0; w < kWaves; ++w) {
+            added += wave_cnt[w][t];
+            wave_cnt[w][t] = 0;
+        }
+        run[t] += added;
+        __syncthreads();
+    }
+}
+
+// bin_start[b] = first position whose key >= b, for b in [0, nbins].
+__global__ void k_starts(const int32_t *__restrict__ keys, int32_t n, int32_t nbins,
+                         int32_t *__restrict__ bin_start)
+{
+    const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (b > nbins)
+        return;
+    int32_t lo = 0, hi = n;
+    while (lo < hi) {
+        const int32_t mid = lo + (hi - lo) / 2;
+        if (keys[mid] < b)
+            lo = mid + 1;
+        else
+            hi = mid;
+    }
+    bin_start[b] = lo;
+}
+
+__global__ void k_gather(const float4 *__restrict__ atoms, const int32_t *__restrict__ idx,
+                         int32_t n, float4 *__restrict__ sorted)
+{
+    const int32_t i = blockIdx.x * kThreads + threadIdx.x;
+    if (i < n)
+        sorted[i] = atoms[idx[i]];
+}
+
+int32_t radix_passes(int64_t nbins)
+{
+    int bits = 0;
+    while (((int64_t)1 << bits) <= nbins)  // keys take values 0 .. nbins
+        ++bits;
+    return (bits + 7) / 8;
+}
+
+unsigned grid_for(int64_t n) { return (unsigned)((n + kThreads - 1) / kThreads); }
+
+}  // namespace
 
 BinLayout bin_layout(int64_t n_atoms, const BinGeometry &g)
 {
     BinLayout L{};
-    auto up = [](size_t v) { return (v + 255) & ~size_t(255); };
-    L.header = 256;
-    L.bin_start = L.header;
-    L.sorted = up(L.bin_start + sizeof(int32_t) * (size_t)(g.nbins() + 1));
-    L.total = up(L.sorted + 16 * (size_t)n_atoms);
+    const size_t n = (size_t)n_atoms;
+    L.n_tiles = (n_atoms + kTileElems - 1) / kTileElems;
+    L.passes = radix_passes(g.nbins());
+    L.header = 0;
+    L.bin_start = 0;
+    L.sorted = up256(sizeof(int32_t) * (size_t)(g.nbins() + 1));
+    L.keys[0] = up256(L.sorted + 16 * n);
+    L.keys[1] = up256(L.keys[0] + 4 * n);
+    L.vals[0] = up256(L.keys[1] + 4 * n);
+    L.vals[1] = up256(L.vals[0] + 4 * n);
+    L.hist = up256(L.vals[1] + 4 * n);
+    L.total = up256(L.hist + sizeof(int32_t) * kDigits * (size_t)L.n_tiles);
     return L;
 }
 
-hipError_t launch_bin_atoms(const float4 *, int64_t, const Lattice &, const BinGeometry &,
-                            const BinLayout &, void *, hipStream_t)
+hipError_t launch_bin_atoms(const float4 *atoms, int64_t n_atoms, const Lattice &lat,
+                            const BinGeometry &g, const BinLayout &L, void *workspace,
+                            hipStream_t stream)
 {
-    return hipErrorNotSupported;
+    (void)lat;
+    char *ws = static_cast<char *>(workspace);
+    const int32_t n = (int32_t)n_atoms;
+    const int32_t nbins = (int32_t)g.nbins();
+    int32_t *bin_start = reinterpret_cast<int32_t *>(ws + L.bin_start);
+    float4 *sorted = reinterpret_cast<float4 *>(ws + L.sorted);
+    int32_t *keys[2] = {reinterpret_cast<int32_t *>(ws + L.keys[0]),
+                        reinterpret_cast<int32_t *>(ws + L.keys[1])};
+    int32_t *vals[2] = {reinterpret_cast<int32_t *>(ws + L.vals[0]),
+                        reinterpret_cast<int32_t *>(ws + L.vals[1])};
+    int32_t *hist = reinterpret_cast<int32_t *>(ws + L.hist);
+
+    if (n > 0) {
+        hipLaunchKernelGGL(k_keys, dim3(grid_for(n)), dim3(kThreads), 0, stream, atoms, n,
+                           g.ax[0].b0, g.ax[1].b0, g.ax[2].b0, g.ax[0].nb, g.ax[1].nb, g.ax[2].nb,
+                           g.bin_size, nbins, keys[0], vals[0]);
+        const int32_t tiles = (int32_t)L.n_tiles;
+        for (int p = 0; p < L.passes; ++p) {
+            const int shift = 8 * p;
+            const int src = p & 1, dst = src ^ 1;
+            hipLaunchKernelGGL(k_hist, dim3(tiles), dim3(kThreads), 0, stream, keys[src], n,
+                               shift, tiles, hist);
+            hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, stream, hist,
+                               (int64_t)kDigits * tiles);
+            hipLaunchKernelGGL(k_scatter, dim3(tiles), dim3(kThreads), 0, stream, keys[src],
+                               vals[src], n, shift, tiles, hist, keys[dst], vals[dst]);
+        }
+        const int fin = L.passes & 1;
+        hipLaunchKernelGGL(k_gather, dim3(grid_for(n)), dim3(kThreads), 0, stream, atoms,
+                           vals[fin], n, sorted);
+        hipLaunchKernelGGL(k_starts, dim3(grid_for((int64_t)nbins + 1)), dim3(kThreads), 0,
+                           stream, keys[fin], n, nbins, bin_start);
+    } else {
+        hipLaunchKernelGGL(k_starts, dim3(grid_for((int64_t)nbins + 1)), dim3(kThreads), 0,
+                           stream, keys[0], 0, nbins, bin_start);
+    }
+    return hipGetLastError();
 }
 
 }  // namespace cpmap

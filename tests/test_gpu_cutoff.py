@@ -1,0 +1,186 @@
+"""GPU parity of the cutoff path against the fp64 oracle.
+
+cpmap_bin_atoms is integer work decided in fp32 (bin coordinate = fl(fl(p -
+b0)/bs), the same operations on both sides): its CSR must equal the oracle's
+stable counting sort bit for bit.  cpmap_cutoff must satisfy
+|V_gpu - V_oracle| <= 1e-5 * S_c at every checked node, S_c = sum over
+r < rc of |q|/r (so nodes with no atom inside the cutoff must be exactly 0).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import direct_coulomb_potential_amd as cpmap
+from direct_coulomb_potential_amd import Lattice
+from direct_coulomb_potential_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the gpu tests need an MI355X")
+    return torch
+
+
+def _bin(torch, atoms_np, lat, bs, rc):
+    atoms = torch.from_numpy(np.ascontiguousarray(atoms_np, dtype=np.float32)).cuda()
+    ws = cpmap.bin_atoms(atoms, lat, bs, rc)
+    starts, srt = cpmap.workspace_views(ws, atoms_np.shape[0], lat, bs, rc)
+    torch.cuda.synchronize()
+    return atoms, ws, starts.cpu().numpy(), srt.cpu().numpy()
+
+
+def _check_csr(torch, atoms_np, lat, bs, rc):
+    _, ws, starts, srt = _bin(torch, atoms_np, lat, bs, rc)
+    o_starts, o_sorted, _ = oracle.bin_atoms(atoms_np, lat.dims, lat.spacing, lat.origin, bs, rc)
+    np.testing.assert_array_equal(starts, o_starts)
+    kept = int(o_starts[-1])
+    assert srt[:kept].tobytes() == o_sorted.tobytes()
+    return ws
+
+
+BIN_CASES = [
+    # (n, lattice, bs, rc, box_lo, box_hi, seed)
+    (1, Lattice(5, 5, 5, 0.5), 1.0, 2.0, (0, 0, 0), (2, 2, 2), 1),
+    (777, Lattice(37, 21, 13, 0.5, (1.0, -2.0, 0.25)), 1.5, 3.0, (-5, -8, -5), (25, 12, 12), 2),
+    (5000, Lattice(30, 30, 30, 0.3, (-4.0, 0.0, 2.0)), 1.0, 2.5, (-8, -4, -2), (8, 13, 14), 3),
+    (70_000, Lattice(64, 48, 40, 0.5), 2.0, 6.0, (-10, -10, -10), (42, 34, 30), 4),
+    (3000, Lattice(200, 200, 200, 0.5), 0.25, 12.0, (0, 0, 0), (100, 100, 100), 5),  # 3 radix passes
+]
+
+
+@pytest.mark.parametrize("case", BIN_CASES, ids=[f"n{c[0]}_bs{c[2]}" for c in BIN_CASES])
+def test_bin_atoms_bit_exact(torch, case):
+    n, lat, bs, rc, lo, hi, seed = case
+    print(f"[bin] n={n} dims={lat.dims} bs={bs} rc={rc}", flush=True)
+    atoms = wl.random_atoms(n, lo, hi, seed=seed)
+    _check_csr(torch, atoms, lat, bs, rc)
+
+
+def test_bin_atoms_edge_cases(torch):
+    """No atoms; every atom in one bin (order kept); atoms on bin faces, outside
+    the halo, and with NaN coordinates (dropped on both sides)."""
+    lat = Lattice(8, 8, 8, 1.0)
+    _check_csr(torch, np.zeros((0, 4), np.float32), lat, 2.0, 3.0)
+    same = wl.random_atoms(5000, (2.0, 2.0, 2.0), (2.5, 2.5, 2.5), seed=6)
+    _check_csr(torch, same, lat, 2.0, 3.0)
+    faces = np.array([[0, 0, 0, 1], [2, 0, 0, 1], [-4, -4, -4, 1], [-4.001, 0, 0, 1],
+                      [13.999, 0, 0, 1], [14, 0, 0, 1], [np.nan, 0, 0, 1], [1e30, 0, 0, 1],
+                      [-1e30, 0, 0, 1], [1.0, 1.0, 1.0, 0.0]], dtype=np.float32)
+    _check_csr(torch, faces, lat, 2.0, 3.0)
+
+
+def test_bin_atoms_config5_bit_exact(torch):
+    w = wl.cutoff_binned()
+    _check_csr(torch, w.atoms, w.lattice, w.bin_size, w.cutoff)
+
+
+def test_bin_atoms_is_deterministic(torch):
+    atoms_np = wl.random_atoms(50_000, (0, 0, 0), (20, 20, 20), seed=7)
+    lat = Lattice(40, 40, 40, 0.5)
+    _, ws1, s1, a1 = _bin(torch, atoms_np, lat, 2.0, 6.0)
+    _, ws2, s2, a2 = _bin(torch, atoms_np, lat, 2.0, 6.0)
+    assert np.array_equal(s1, s2) and a1.tobytes() == a2.tobytes()
+
+
+def _parity(Vg, Vo, S, label):
+    err = np.abs(Vg.astype(np.float64) - Vo)
+    bad = ~(err <= TOL * S)
+    if bad.any():
+        i = int(np.argmax(np.where(bad, err, -1)))
+        raise AssertionError(f"{label}: {bad.sum()} nodes out of bound; node {i}: gpu {Vg[i]!r} "
+                             f"oracle {Vo[i]!r} S {S[i]!r}")
+    ratio = err / np.where(S > 0, S, 1.0)
+    return float(ratio.max()) if ratio.size else 0.0
+
+
+CUT_CASES = [
+    (1, Lattice(9, 9, 9, 0.5), 1.0, 2.0, (1, 1, 1), (3, 3, 3), 11),
+    (500, Lattice(19, 13, 11, 0.5), 1.0, 2.0, (-3, -3, -3), (12, 9, 8), 12),
+    (2000, Lattice(37, 21, 13, 0.5, (1.0, -2.0, 0.25)), 1.5, 3.0, (-5, -8, -5), (25, 12, 12), 13),
+    (4000, Lattice(30, 30, 30, 0.3, (-4.0, 0.0, 2.0)), 1.0, 2.5, (-8, -4, -2), (8, 13, 14), 14),
+    (20_000, Lattice(48, 40, 33, 0.5), 4.0, 12.0, (-14, -14, -14), (38, 34, 30), 15),
+    (6000, Lattice(24, 24, 24, 0.5), 0.5, 3.0, (-4, -4, -4), (16, 16, 16), 16),  # many rows per tile
+]
+
+
+@pytest.mark.parametrize("case", CUT_CASES, ids=[f"n{c[0]}_{c[1].nx}x{c[1].ny}x{c[1].nz}_bs{c[2]}" for c in CUT_CASES])
+def test_cutoff_small_all_nodes(torch, case):
+    n, lat, bs, rc, lo, hi, seed = case
+    print(f"[cutoff] n={n} dims={lat.dims} bs={bs} rc={rc}", flush=True)
+    atoms_np = wl.random_atoms(n, lo, hi, seed=seed)
+    atoms = torch.from_numpy(atoms_np).cuda()
+    ws = cpmap.bin_atoms(atoms, lat, bs, rc)
+    V = cpmap.cutoff(ws, n, lat, bs, rc).cpu().numpy().reshape(-1)
+    Vo, S = oracle.cutoff(atoms_np, lat.dims, lat.spacing, lat.origin, rc, with_scale=True)
+    _parity(V, Vo, S, f"n={n} dims={lat.dims}")
+
+
+def test_cutoff_zero_far_from_atoms(torch):
+    """Nodes farther than rc from every atom are exactly 0, including whole
+    tiles whose neighbourhood is empty."""
+    atoms_np = wl.random_atoms(400, (0, 0, 0), (6, 6, 6), seed=17)
+    lat = Lattice(40, 16, 16, 0.5)
+    atoms = torch.from_numpy(atoms_np).cuda()
+    ws = cpmap.bin_atoms(atoms, lat, 1.0, 3.0)
+    V = cpmap.cutoff(ws, 400, lat, 1.0, 3.0).cpu().numpy().reshape(-1)
+    Vo, S = oracle.cutoff(atoms_np, lat.dims, lat.spacing, lat.origin, 3.0, with_scale=True)
+    assert np.all(V[S == 0] == 0.0) and (S == 0).sum() > 1000
+    _parity(V, Vo, S, "far")
+
+
+def test_cutoff_no_atoms(torch):
+    lat = Lattice(10, 10, 10, 0.5)
+    ws = cpmap.bin_atoms(torch.zeros((0, 4), device="cuda"), lat, 1.0, 2.0)
+    out = torch.full((10, 10, 10), 3.0, device="cuda")
+    V = cpmap.cutoff(ws, 0, lat, 1.0, 2.0, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(V == 0).item()
+
+
+def test_cutoff_config5_checked_nodes(torch):
+    w = wl.cutoff_binned()
+    lat = w.lattice
+    atoms = torch.from_numpy(w.atoms).cuda()
+    ws = cpmap.bin_atoms(atoms, lat, w.bin_size, w.cutoff)
+    V = cpmap.cutoff(ws, w.n_atoms, lat, w.bin_size, w.cutoff).cpu().numpy().reshape(-1)
+    nodes = wl.checked_nodes(lat)
+    Vo, S = oracle.cutoff(w.atoms, lat.dims, lat.spacing, lat.origin, w.cutoff, nodes=nodes,
+                          with_scale=True)
+    worst = _parity(V[nodes], Vo, S, w.name)
+    print(f"{w.name}: {nodes.size} nodes, worst |err|/S = {worst:.3e}")
+
+
+def test_cutoff_is_deterministic_and_checks_geometry(torch):
+    atoms_np = wl.random_atoms(30_000, (0, 0, 0), (20, 20, 20), seed=18)
+    lat = Lattice(40, 40, 40, 0.5)
+    atoms = torch.from_numpy(atoms_np).cuda()
+    ws = cpmap.bin_atoms(atoms, lat, 2.0, 6.0)
+    a = cpmap.cutoff(ws, 30_000, lat, 2.0, 6.0).clone()
+    b = cpmap.cutoff(ws, 30_000, lat, 2.0, 6.0)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    with pytest.raises(cpmap.CpmapError) as e:
+        cpmap.cutoff(ws, 30_000, Lattice(40, 40, 41, 0.5), 2.0, 6.0)
+    assert e.value.status in (3, 4)  # ENOSPC or EGEOM: never a launch on a foreign layout
+    with pytest.raises(cpmap.CpmapError):
+        cpmap.cutoff(ws, 29_999, lat, 2.0, 6.0)
+
+
+def test_cutoff_matches_direct_minus_gamma_for_huge_cutoff(torch):
+    """With rc beyond every distance the cutoff path keeps every atom: compare
+    with the oracle's cutoff sum, which then differs from the direct sum only
+    by the smoothing polynomial."""
+    atoms_np = wl.random_atoms(3000, (0, 0, 0), (8, 8, 8), seed=19)
+    lat = Lattice(16, 16, 16, 0.5)
+    atoms = torch.from_numpy(atoms_np).cuda()
+    rc = 40.0
+    ws = cpmap.bin_atoms(atoms, lat, 8.0, rc)
+    V = cpmap.cutoff(ws, 3000, lat, 8.0, rc).cpu().numpy().reshape(-1)
+    Vo, S = oracle.cutoff(atoms_np, lat.dims, lat.spacing, lat.origin, rc, with_scale=True)
+    _parity(V, Vo, S, "huge rc")
