@@ -39,8 +39,11 @@ def parse():
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-cutoff", action="store_true")
-    p.add_argument("--only", choices=["direct", "cutoff"], default=None,
-                   help="time one path only (for profiler runs)")
+    p.add_argument("--only", choices=["direct", "cutoff", "copy"], default=None,
+                   help="time one path only (for profiler runs); 'copy' runs the plain "
+                        "256 MiB copy kernel that calibrates the HBM byte counters")
+    p.add_argument("--no-direct-compare", action="store_true",
+                   help="skip the direct sum on the cutoff atoms (for profiler runs)")
     return p.parse_args()
 
 
@@ -67,7 +70,8 @@ def cpu_baseline(oracle, w, target_s):
     """The fp64 oracle, as it stands, on a bounded node sample of the workload."""
     lat = w.lattice
     rng = np.random.default_rng(1234)
-    probe = rng.integers(0, lat.n_points, size=64, dtype=np.int64)
+    probe = rng.integers(0, lat.n_points, size=1024, dtype=np.int64)
+    oracle.direct(w.atoms, lat.dims, lat.spacing, lat.origin, nodes=probe[:64])  # thread start-up
     t0 = time.perf_counter()
     oracle.direct(w.atoms, lat.dims, lat.spacing, lat.origin, nodes=probe)
     rate = probe.size * w.n_atoms / max(time.perf_counter() - t0, 1e-6)
@@ -104,6 +108,15 @@ def main():
     cpmap.library()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.only == "copy":
+        # calibration: one elementwise kernel reading and writing 256 MiB each
+        a = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        torch.mul(a, 2.0, out=b)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": a.numel() * 4, "copy_bytes_written": b.numel() * 4}))
+        return
 
     w = wl.large_direct()
     lat = w.lattice
@@ -191,11 +204,14 @@ def bench_cutoff(torch, cpmap, wl, dev, args):
     _, per_bin = time_launches(torch, run_bin, steps, args.warmup)
     _, per_cut = time_launches(torch, run_cut, steps, args.warmup)
     wall_e2e, _ = time_launches(torch, run_both, steps, args.warmup)
-    Vd = torch.empty_like(V)
-    _, per_dir = time_launches(torch, lambda: cpmap.direct(atoms, lat, out=Vd), 2, 1)
     cut_ms = statistics.median(per_cut)
     bin_ms = statistics.median(per_bin)
-    dir_ms = statistics.median(per_dir)
+    if args.no_direct_compare:
+        dir_ms = float("nan")
+    else:
+        Vd = torch.empty_like(V)
+        _, per_dir = time_launches(torch, lambda: cpmap.direct(atoms, lat, out=Vd), 2, 1)
+        dir_ms = statistics.median(per_dir)
     bytes_alg = 16 * w.n_atoms + 4 * lat.n_points
     return {
         "workload": w.name,

@@ -18,10 +18,15 @@
 //  - the spans' atoms are staged into LDS (the lecture's "fetch bins of data
 //    into shared memory", one bin at a time there; all spans at once here, in
 //    chunks of kStage atoms when the neighbourhood is larger);
-//  - each lane owns kNx consecutive nodes of one x-row, reads every staged
-//    atom as an LDS broadcast, shares dy and dz across its nodes, and adds the
-//    masked term: outside the cutoff the charge is replaced by exactly 0, so
-//    nodes beyond rc of every atom get exactly 0;
+//  - each wave owns an 8x8x4 slab of the tile and keeps, in an LDS index list,
+//    only the staged atoms within rc of its slab's node box (one atom per
+//    lane tested, ballot + prefix count), which removes about 40% of the
+//    examined pairs at 4 A bins; this is the lecture's "sphere of bins" idea
+//    applied per wave at atom granularity;
+//  - each lane owns kNx consecutive nodes of one x-row, reads its wave's
+//    listed atoms as LDS broadcasts, shares dy and dz across its nodes, and
+//    adds the masked term: outside the cutoff the charge is replaced by
+//    exactly 0, so nodes beyond rc of every atom get exactly 0;
 //  - V is written once per node, x-fastest.
 #include <cmath>
 
@@ -161,24 +166,48 @@ struct CutoffParams {
     float gc0, gc1, gc2;
 };
 
+constexpr int kWaves = kThreads / 64;
+
+// One staged atom against this lane's kNx nodes.
+__device__ __forceinline__ void add_atom(const float4 at, const float (&x)[kNx], float y, float z,
+                                         const CutoffParams &P, float (&acc)[kNx])
+{
+    const float dy = y - at.y;
+    const float dz = z - at.z;
+    const float yz2 = fmaf(dy, dy, dz * dz);
+#pragma unroll
+    for (int c = 0; c < kNx; ++c) {
+        const float dx = x[c] - at.x;
+        const float r2 = fmaf(dx, dx, yz2);
+        const float rs = __builtin_amdgcn_rsqf(r2);
+        const float g = fmaf(fmaf(r2, P.gc2, P.gc1), r2, P.gc0);
+        const float qm = r2 < P.rc2 ? at.w : 0.0f;
+        acc[c] = fmaf(qm, rs - g, acc[c]);
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void cutoff_kernel(CutoffParams P,
                                                           const int32_t *__restrict__ bin_start,
                                                           const float4 *__restrict__ sorted,
                                                           int32_t n_sorted, float *__restrict__ V)
 {
     __shared__ float4 stage[kStage];
+    __shared__ uint16_t wave_list[kWaves][kStage];
     __shared__ int32_t span_src[kMaxRows];
     __shared__ int32_t span_off[kMaxRows + 1];
     __shared__ int32_t scan_tmp[kThreads];
 
     const int t = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(t / 64);
+    const int lane = t % 64;
     const int32_t tile = blockIdx.x;
     const int32_t tx = tile % P.tiles[0];
     const int32_t ty = (tile / P.tiles[0]) % P.tiles[1];
     const int32_t tz = tile / (P.tiles[0] * P.tiles[1]);
     const TileRows T = tile_rows(tx, ty, tz, P.n, P.h, P.o, P.b0, P.nb, P.bs, P.rc);
 
-    // This lane's nodes: an x-run of kNx nodes in one row of one plane.
+    // This lane's nodes: an x-run of kNx nodes in one row of one plane; the
+    // wave's 64 lanes cover 8 x 8 x (kTile / kWaves) nodes.
     const int32_t xs = t % (kTile / kNx);
     const int32_t yl = (t / (kTile / kNx)) % kTile;
     const int32_t zl = t / (kTile / kNx * kTile);
@@ -195,6 +224,19 @@ __global__ __launch_bounds__(kThreads) void cutoff_kernel(CutoffParams P,
 #pragma unroll
     for (int c = 0; c < kNx; ++c)
         acc[c] = 0.0f;
+
+    // The wave's node box (nodes past the lattice edge included: they are
+    // computed and dropped, so the box only needs to contain the live ones).
+    constexpr int kSlab = kTile / kWaves;
+    const float wlo[3] = {node_coord((int64_t)tx * kTile, P.h, P.o[0]),
+                          node_coord((int64_t)ty * kTile, P.h, P.o[1]),
+                          node_coord((int64_t)tz * kTile + wave * kSlab, P.h, P.o[2])};
+    const float whi[3] = {node_coord((int64_t)tx * kTile + kTile - 1, P.h, P.o[0]),
+                          node_coord((int64_t)ty * kTile + kTile - 1, P.h, P.o[1]),
+                          node_coord((int64_t)tz * kTile + wave * kSlab + kSlab - 1, P.h,
+                                     P.o[2])};
+    // a slightly widened radius keeps the list conservative against rounding
+    const float keep2 = P.rc2 * 1.0001f;
 
     for (int32_t row0 = 0; row0 < T.nrows; row0 += kMaxRows) {
         const int32_t rows = T.nrows - row0 < kMaxRows ? T.nrows - row0 : kMaxRows;
@@ -233,12 +275,13 @@ __global__ __launch_bounds__(kThreads) void cutoff_kernel(CutoffParams P,
             span_off[r] = run;
             run += c;
         }
-        const int32_t total = scan_tmp[kThreads - 1];
+        const int32_t total = __builtin_amdgcn_readfirstlane(scan_tmp[kThreads - 1]);
         if (t == 0)
             span_off[rows] = total;
         __syncthreads();
 
-        // 3. stage the spans' atoms in chunks and sweep them
+        // 3. stage the spans' atoms in chunks; each wave lists the atoms near
+        //    its slab and sweeps them
         for (int32_t c0 = 0; c0 < total; c0 += kStage) {
             const int32_t m = total - c0 < kStage ? total - c0 : kStage;
             for (int32_t e = t; e < m; e += kThreads) {
@@ -254,21 +297,43 @@ __global__ __launch_bounds__(kThreads) void cutoff_kernel(CutoffParams P,
                 stage[e] = sorted[span_src[a] + (g - span_off[a])];
             }
             __syncthreads();
-            for (int32_t e = 0; e < m; ++e) {
-                const float4 at = stage[e];
-                const float dy = y - at.y;
-                const float dz = z - at.z;
-                const float yz2 = fmaf(dy, dy, dz * dz);
-#pragma unroll
-                for (int c = 0; c < kNx; ++c) {
-                    const float dx = x[c] - at.x;
-                    const float r2 = fmaf(dx, dx, yz2);
-                    const float rs = __builtin_amdgcn_rsqf(r2);
-                    const float g = fmaf(fmaf(r2, P.gc2, P.gc1), r2, P.gc0);
-                    const float qm = r2 < P.rc2 ? at.w : 0.0f;
-                    acc[c] = fmaf(qm, rs - g, acc[c]);
+            int32_t listed = 0;
+            for (int32_t e0 = 0; e0 < m; e0 += 64) {
+                const int32_t e = e0 + lane;
+                bool near = false;
+                if (e < m) {
+                    const float4 at = stage[e];
+                    const float gx = fmaxf(fmaxf(wlo[0] - at.x, at.x - whi[0]), 0.0f);
+                    const float gy = fmaxf(fmaxf(wlo[1] - at.y, at.y - whi[1]), 0.0f);
+                    const float gz = fmaxf(fmaxf(wlo[2] - at.z, at.z - whi[2]), 0.0f);
+                    near = fmaf(gx, gx, fmaf(gy, gy, gz * gz)) < keep2;
                 }
+                const uint64_t vote = __ballot(near);
+                if (near) {
+                    const uint64_t below = lane == 0 ? 0ull : (vote & (~0ull >> (64 - lane)));
+                    wave_list[wave][listed + __popcll(below)] = (uint16_t)e;
+                }
+                listed += __popcll(vote);
             }
+            listed = __builtin_amdgcn_readfirstlane(listed);
+            // the list is written and read by this wave only
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const uint16_t *list = wave_list[wave];
+            int32_t i = 0;
+            for (; i + 4 <= listed; i += 4) {
+                const float4 a0 = stage[list[i + 0]];
+                const float4 a1 = stage[list[i + 1]];
+                const float4 a2 = stage[list[i + 2]];
+                const float4 a3 = stage[list[i + 3]];
+                add_atom(a0, x, y, z, P, acc);
+                add_atom(a1, x, y, z, P, acc);
+                add_atom(a2, x, y, z, P, acc);
+                add_atom(a3, x, y, z, P, acc);
+            }
+            for (; i < listed; ++i)
+                add_atom(stage[list[i]], x, y, z, P, acc);
             __syncthreads();
         }
     }

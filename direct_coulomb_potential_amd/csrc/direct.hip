@@ -23,6 +23,10 @@
 //    result deterministic, and W fills the 1024 SIMDs for small lattices.
 //  - nodes are stored x-fastest, V[(k*ny + j)*nx + i] (section 18.4) from the
 //    LDS total; lanes adjacent in x write adjacent 4*CX-byte runs.
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+
 #include "cpmap_internal.h"
 
 namespace cpmap {
@@ -51,14 +55,10 @@ __device__ __forceinline__ void accumulate_atom(const float4 a, const float (&x)
 #pragma unroll
         for (int d = 0; d < CY; ++d) {
             const float yz2 = fmaf(dy[d], dy[d], dz2);
-            float rs[CX];
-#pragma unroll
-            for (int c = 0; c < CX; ++c)
-                rs[c] = __builtin_amdgcn_rsqf(fmaf(dx[c], dx[c], yz2));
 #pragma unroll
             for (int c = 0; c < CX; ++c) {
                 float &v = acc[(e * CY + d) * CX + c];
-                v = fmaf(a.w, rs[c], v);
+                v = fmaf(a.w, __builtin_amdgcn_rsqf(fmaf(dx[c], dx[c], yz2)), v);
             }
         }
     }
@@ -179,49 +179,68 @@ struct Variant {
 #define CPMAP_VARIANT(CX, CY, CZ, W) Variant{CX, CY, CZ, W, direct_kernel<CX, CY, CZ, W>}
 
 const Variant kVariants[] = {
-    CPMAP_VARIANT(8, 8, 2, 4),  CPMAP_VARIANT(8, 8, 2, 8),  CPMAP_VARIANT(8, 4, 4, 8),
-    CPMAP_VARIANT(8, 4, 2, 4),  CPMAP_VARIANT(8, 4, 2, 8),  CPMAP_VARIANT(4, 4, 4, 8),
-    CPMAP_VARIANT(4, 4, 2, 8),  CPMAP_VARIANT(4, 4, 2, 16), CPMAP_VARIANT(4, 4, 1, 16),
-    CPMAP_VARIANT(2, 2, 1, 16), CPMAP_VARIANT(1, 1, 1, 16),
+    CPMAP_VARIANT(8, 8, 2, 4),  CPMAP_VARIANT(8, 8, 2, 8),  CPMAP_VARIANT(8, 4, 2, 4),
+    CPMAP_VARIANT(8, 4, 2, 8),  CPMAP_VARIANT(4, 4, 2, 8),  CPMAP_VARIANT(4, 4, 2, 16),
+    CPMAP_VARIANT(4, 4, 1, 16), CPMAP_VARIANT(2, 2, 1, 16), CPMAP_VARIANT(1, 1, 1, 16),
 };
+constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Estimated time of a variant in units of (pair issue slots / SIMD), from the
-// blocking's shared work, its ragged waste, and how evenly its waves spread
-// over 1024 SIMDs at the occupancy its registers allow.
-double variant_cost(const Variant &v, const Lattice &lat, int64_t n_atoms)
+// Waves of one variant that a SIMD holds at once, from the runtime's
+// occupancy calculator (registers and LDS of the compiled kernel); cached.
+int waves_per_simd(int idx)
 {
-    const int64_t bx = ceil_div(lat.n[0], v.cx), by = ceil_div(lat.n[1], v.cy),
-                  bz = ceil_div(lat.n[2], v.cz);
-    const int64_t strips = bx * by * bz;
+    static std::atomic<int> cache[kNumVariants];
+    int v = cache[idx].load(std::memory_order_relaxed);
+    if (v > 0)
+        return v;
+    const Variant &var = kVariants[idx];
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, var.kernel, kWave * var.w, 0) !=
+            hipSuccess ||
+        blocks <= 0)
+        blocks = 1;
+    v = std::max(1, blocks * var.w / 4);
+    cache[idx].store(v, std::memory_order_relaxed);
+    return v;
+}
+
+// Modelled run time of a variant, in VALU issue slots of the busiest SIMD.
+//  - a pair costs 4 slots (fma, half-rate v_rsq_f32, fma) plus the blocking's
+//    shared per-atom work;
+//  - workgroups spread evenly over the 256 CUs and each puts W/4 waves on
+//    every SIMD of its CU; a SIMD runs `occ` waves at once, and needs two
+//    resident waves to keep its VALU busy, so a lone wave runs at half rate.
+double variant_cost(int idx, const Lattice &lat, int64_t n_atoms)
+{
+    const Variant &v = kVariants[idx];
+    const int64_t strips = ceil_div(lat.n[0], v.cx) * ceil_div(lat.n[1], v.cy) *
+                           ceil_div(lat.n[2], v.cz);
+    const int64_t groups = ceil_div(strips, kWave);
     const double np = v.cx * v.cy * v.cz;
     const double per_pair = 4.0 + (v.cx + v.cy + 2.0 * v.cz + v.cy * v.cz) / np;
-    const int64_t groups = ceil_div(strips, kWave);
-    const double atoms_per_wave = std::ceil((double)n_atoms / v.w);
-    // one wave's work, plus a fixed start-up and reduction cost per wave
-    const double wave_work = atoms_per_wave * np * per_pair + 2000.0 + 40.0 * np * v.w;
-    const int per_simd = np >= 128 ? 2 : (np >= 64 ? 3 : 4);
-    const double slots = 1024.0 * per_simd;
-    const double waves = (double)groups * v.w;
-    // waves sharing a SIMD split its issue rate, so time ~ waves per SIMD
-    const double depth = std::ceil(waves / slots) * per_simd;
-    const double busiest = std::min(depth, std::ceil(waves / 1024.0));
-    return busiest * wave_work;
+    const double wave_work = std::ceil((double)n_atoms / v.w) * np * per_pair + 64.0 * np;
+    const int64_t per_simd = ceil_div(groups, 256) * std::max(1, v.w / 4);
+    const int occ = waves_per_simd(idx);
+    double units = 0.0;
+    for (int64_t left = per_simd; left > 0; left -= occ)
+        units += (double)std::max<int64_t>(std::min<int64_t>(left, occ), 2);
+    return units * wave_work;
 }
 
 const Variant &pick_variant(const Lattice &lat, int64_t n_atoms)
 {
-    const Variant *best = &kVariants[0];
-    double best_cost = variant_cost(*best, lat, n_atoms);
-    for (const Variant &v : kVariants) {
-        const double c = variant_cost(v, lat, n_atoms);
+    int best = 0;
+    double best_cost = variant_cost(0, lat, n_atoms);
+    for (int i = 1; i < kNumVariants; ++i) {
+        const double c = variant_cost(i, lat, n_atoms);
         if (c < best_cost) {
             best_cost = c;
-            best = &v;
+            best = i;
         }
     }
-    return *best;
+    return kVariants[best];
 }
 
 }  // namespace
