@@ -30,6 +30,24 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 FLOP_PER_EVAL = 10
 
 
+def measured_traffic(profile: str, source: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None
+    when the kernel source has changed since the counters were taken."""
+    import hashlib
+    import re
+    try:
+        with open(os.path.join(ROOT, "profiles", profile)) as f:
+            block = re.search(r"```json\n(.*?)\n```", f.read(), re.S)
+        rec = json.loads(block.group(1))
+        with open(os.path.join(ROOT, source), "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, AttributeError, ValueError):
+        return None
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -156,7 +174,9 @@ def main():
             "peak": PEAK_FP32_TFLOPS,
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_FP32_TFLOPS,
-            "traffic": None,
+            "traffic": measured_traffic("direct_kernel_200cube_200k.md",
+                                        "direct_coulomb_potential_amd/csrc/direct.hip"),
+            "traffic_unit": "bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated)",
             "kernel": "direct_kernel",
             "kernel_ms_mean": kern_ms,
             "kernel_ms_median": statistics.median(per),
@@ -222,6 +242,8 @@ def bench_cutoff(torch, cpmap, wl, dev, args):
         "direct_same_atoms_ms": dir_ms,
         "speedup_vs_direct": dir_ms / (cut_ms + bin_ms),
         "hbm_gbs_algorithmic": bytes_alg / (cut_ms * 1e-3) / 1e9,
+        "hbm_traffic_bytes_per_launch": measured_traffic(
+            "cutoff_kernel_200cube_100k_rc12.md", "direct_coulomb_potential_amd/csrc/cutoff.hip"),
         "direct_equivalent_G_evals_per_s": w.pairs / ((cut_ms + bin_ms) * 1e-3) / 1e9,
     }
 
