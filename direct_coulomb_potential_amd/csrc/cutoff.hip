@@ -25,8 +25,10 @@
 //    applied per wave at atom granularity;
 //  - each lane owns kNx consecutive nodes of one x-row, reads its wave's
 //    listed atoms as LDS broadcasts, shares dy and dz across its nodes, and
-//    adds the masked term: outside the cutoff the charge is replaced by
-//    exactly 0, so nodes beyond rc of every atom get exactly 0;
+//    adds the term with r^2 clamped to the largest value <= rc^2 at which the
+//    fp32 term is exactly 0 (found in the prologue; the select-based mask
+//    q -> 0 is the fallback), so atoms beyond the cutoff add exactly nothing
+//    and nodes beyond rc of every atom get exactly 0;
 //  - V is written once per node, x-fastest.
 #include <cmath>
 
@@ -168,7 +170,11 @@ struct CutoffParams {
 
 constexpr int kWaves = kThreads / 64;
 
-// One staged atom against this lane's kNx nodes.
+// One staged atom against this lane's kNx nodes.  With kClamp, r^2 is
+// clamped to P.rc2, for which the kernel has checked that the fp32 term is
+// exactly 0 (so atoms beyond the cutoff add exactly nothing); otherwise the
+// charge is replaced by 0 outside the cutoff.
+template <bool kClamp>
 __device__ __forceinline__ void add_atom(const float4 at, const float (&x)[kNx], float y, float z,
                                          const CutoffParams &P, float (&acc)[kNx])
 {
@@ -178,15 +184,66 @@ __device__ __forceinline__ void add_atom(const float4 at, const float (&x)[kNx],
 #pragma unroll
     for (int c = 0; c < kNx; ++c) {
         const float dx = x[c] - at.x;
-        const float r2 = fmaf(dx, dx, yz2);
-        const float rs = __builtin_amdgcn_rsqf(r2);
-        const float g = fmaf(fmaf(r2, P.gc2, P.gc1), r2, P.gc0);
-        const float qm = r2 < P.rc2 ? at.w : 0.0f;
-        acc[c] = fmaf(qm, rs - g, acc[c]);
+        if constexpr (kClamp) {
+            const float r2 = fminf(fmaf(dx, dx, yz2), P.rc2);
+            const float rs = __builtin_amdgcn_rsqf(r2);
+            const float g = fmaf(fmaf(r2, P.gc2, P.gc1), r2, P.gc0);
+            acc[c] = fmaf(at.w, rs - g, acc[c]);
+        } else {
+            const float r2 = fmaf(dx, dx, yz2);
+            const float rs = __builtin_amdgcn_rsqf(r2);
+            const float g = fmaf(fmaf(r2, P.gc2, P.gc1), r2, P.gc0);
+            const float qm = r2 < P.rc2 ? at.w : 0.0f;
+            acc[c] = fmaf(qm, rs - g, acc[c]);
+        }
     }
 }
 
-__global__ __launch_bounds__(kThreads) void cutoff_kernel(CutoffParams P,
+// The same fp32 term as add_atom evaluates, at r^2 = r2.
+__device__ __forceinline__ float term_at(float r2, const CutoffParams &P)
+{
+    return __builtin_amdgcn_rsqf(r2) - fmaf(fmaf(r2, P.gc2, P.gc1), r2, P.gc0);
+}
+
+// Largest r^2 <= rc^2 (within kClampSearch ulps) at which the fp32 term is
+// exactly 0, or 0 if there is none.  The term vanishes to third order at rc,
+// so it is a few ulps of 1/rc around rc^2 and some nearby r^2 rounds it to 0;
+// atoms between that r^2 and rc^2 contribute O((ulp/rc)^3) in exact
+// arithmetic, far below fp32 resolution.
+constexpr int kClampSearch = 64;
+
+__device__ inline float exact_zero_clamp(const CutoffParams &P)
+{
+    uint32_t bits = __float_as_uint(P.rc2);
+    for (int k = 0; k < kClampSearch; ++k, --bits) {
+        const float r2 = __uint_as_float(bits);
+        if (term_at(r2, P) == 0.0f)
+            return r2;
+    }
+    return 0.0f;
+}
+
+template <bool kClamp>
+__device__ __forceinline__ void sweep(const float4 *stage, const uint16_t *list, int32_t listed,
+                                      const float (&x)[kNx], float y, float z,
+                                      const CutoffParams &P, float (&acc)[kNx])
+{
+    int32_t i = 0;
+    for (; i + 4 <= listed; i += 4) {
+        const float4 a0 = stage[list[i + 0]];
+        const float4 a1 = stage[list[i + 1]];
+        const float4 a2 = stage[list[i + 2]];
+        const float4 a3 = stage[list[i + 3]];
+        add_atom<kClamp>(a0, x, y, z, P, acc);
+        add_atom<kClamp>(a1, x, y, z, P, acc);
+        add_atom<kClamp>(a2, x, y, z, P, acc);
+        add_atom<kClamp>(a3, x, y, z, P, acc);
+    }
+    for (; i < listed; ++i)
+        add_atom<kClamp>(stage[list[i]], x, y, z, P, acc);
+}
+
+__global__ __launch_bounds__(kThreads) void cutoff_kernel(CutoffParams P0,
                                                           const int32_t *__restrict__ bin_start,
                                                           const float4 *__restrict__ sorted,
                                                           int32_t n_sorted, float *__restrict__ V)
@@ -196,6 +253,14 @@ __global__ __launch_bounds__(kThreads) void cutoff_kernel(CutoffParams P,
     __shared__ int32_t span_src[kMaxRows];
     __shared__ int32_t span_off[kMaxRows + 1];
     __shared__ int32_t scan_tmp[kThreads];
+
+    // Clamp r^2 where a clamp value with an exactly-zero term exists.
+    CutoffParams P = P0;
+    const float clamp =
+        __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(exact_zero_clamp(P0))));
+    const bool use_clamp = clamp > 0.0f;
+    if (use_clamp)
+        P.rc2 = clamp;
 
     const int t = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(t / 64);
@@ -236,7 +301,7 @@ __global__ __launch_bounds__(kThreads) void cutoff_kernel(CutoffParams P,
                           node_coord((int64_t)tz * kTile + wave * kSlab + kSlab - 1, P.h,
                                      P.o[2])};
     // a slightly widened radius keeps the list conservative against rounding
-    const float keep2 = P.rc2 * 1.0001f;
+    const float keep2 = P0.rc2 * 1.0001f;
 
     for (int32_t row0 = 0; row0 < T.nrows; row0 += kMaxRows) {
         const int32_t rows = T.nrows - row0 < kMaxRows ? T.nrows - row0 : kMaxRows;
@@ -320,20 +385,10 @@ __global__ __launch_bounds__(kThreads) void cutoff_kernel(CutoffParams P,
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            const uint16_t *list = wave_list[wave];
-            int32_t i = 0;
-            for (; i + 4 <= listed; i += 4) {
-                const float4 a0 = stage[list[i + 0]];
-                const float4 a1 = stage[list[i + 1]];
-                const float4 a2 = stage[list[i + 2]];
-                const float4 a3 = stage[list[i + 3]];
-                add_atom(a0, x, y, z, P, acc);
-                add_atom(a1, x, y, z, P, acc);
-                add_atom(a2, x, y, z, P, acc);
-                add_atom(a3, x, y, z, P, acc);
-            }
-            for (; i < listed; ++i)
-                add_atom(stage[list[i]], x, y, z, P, acc);
+            if (use_clamp)
+                sweep<true>(stage, wave_list[wave], listed, x, y, z, P, acc);
+            else
+                sweep<false>(stage, wave_list[wave], listed, x, y, z, P, acc);
             __syncthreads();
         }
     }
