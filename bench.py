@@ -157,7 +157,12 @@ def main():
     if args.only in (None, "direct"):
         atoms = torch.from_numpy(w.atoms).to(dev)
         V = torch.empty((lat.nz, lat.ny, lat.nx), dtype=torch.float32, device=dev)
-        fn = lambda: cpmap.direct(atoms, lat, out=V)  # noqa: E731
+        ws_bytes = cpmap.direct_workspace_bytes(w.n_atoms, lat)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        plan = cpmap.direct_plan(w.n_atoms, lat, True)
+        result["config"]["plan"] = {"nodes_per_lane": list(plan[:3]), "waves_per_workgroup": plan[3],
+                                    "atom_parts": plan[4], "workspace_bytes": ws_bytes}
+        fn = lambda: cpmap.direct(atoms, lat, out=V, workspace=ws)  # noqa: E731
         wall, per = time_launches(torch, fn, args.steps, args.warmup)
         ms_step = wall / args.steps * 1e3
         kern_ms = statistics.mean(per)
@@ -177,13 +182,13 @@ def main():
             "traffic": measured_traffic("direct_kernel_200cube_200k.md",
                                         "direct_coulomb_potential_amd/csrc/direct.hip"),
             "traffic_unit": "bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated)",
-            "kernel": "direct_kernel",
+            "kernel": "direct_kernel (+ sum_parts, the partial-map add, inside the same events)",
             "kernel_ms_mean": kern_ms,
             "kernel_ms_median": statistics.median(per),
             "kernel_ms_min": min(per),
             "flop_per_eval": FLOP_PER_EVAL,
         }
-        del atoms, V
+        del atoms, V, ws
 
     if not args.no_cutoff and args.only in (None, "cutoff"):
         result["cutoff"] = bench_cutoff(torch, cpmap, wl, dev, args)
@@ -230,7 +235,10 @@ def bench_cutoff(torch, cpmap, wl, dev, args):
         dir_ms = float("nan")
     else:
         Vd = torch.empty_like(V)
-        _, per_dir = time_launches(torch, lambda: cpmap.direct(atoms, lat, out=Vd), 2, 1)
+        wsd = torch.empty(max(cpmap.direct_workspace_bytes(w.n_atoms, lat), 1), dtype=torch.uint8,
+                          device=dev)
+        _, per_dir = time_launches(torch, lambda: cpmap.direct(atoms, lat, out=Vd, workspace=wsd),
+                                   2, 1)
         dir_ms = statistics.median(per_dir)
     bytes_alg = 16 * w.n_atoms + 4 * lat.n_points
     return {

@@ -22,7 +22,7 @@ from typing import Optional, Tuple
 from .workloads import Lattice
 
 __all__ = [
-    "Lattice", "CpmapError", "direct", "bin_atoms", "cutoff", "bin_workspace_bytes",
+    "Lattice", "CpmapError", "direct", "direct_workspace_bytes", "direct_plan", "bin_atoms", "cutoff", "bin_workspace_bytes",
     "bin_grid", "workspace_layout", "workspace_views", "neighbor_spans", "library",
     "library_path", "header_functions", "STATUS",
 ]
@@ -51,6 +51,10 @@ _SIGNATURES = {
     "cpmap_version": (_i32, []),
     "cpmap_status_str": (ctypes.c_char_p, [_i32]),
     "cpmap_direct": (_i32, [_vp, _i64, *_LAT, _vp, _vp]),
+    "cpmap_direct_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32]),
+    "cpmap_direct_with_workspace": (_i32, [_vp, _i64, *_LAT, _vp, _vp, _sz, _vp]),
+    "cpmap_direct_plan": (_i32, [_i64, _i32, _i32, _i32, _i32, ctypes.POINTER(_i32)]),
+    "cpmap_direct_occupancy_check": (_i32, []),
     "cpmap_bin_workspace_bytes": (_sz, [_i64, *_LAT, _f32, _f32]),
     "cpmap_bin_grid": (_i32, [*_LAT, _f32, _f32, ctypes.POINTER(_i32)]),
     "cpmap_bin_atoms": (_i32, [_vp, _i64, *_LAT, _f32, _f32, _vp, _sz, _vp]),
@@ -137,14 +141,49 @@ def _out(lat: Lattice, device, out):
     return out
 
 
-def direct(atoms, lat: Lattice, out=None):
-    """Direct Coulomb sum at every node; returns V with shape (nz, ny, nx) (x fastest)."""
+def direct_workspace_bytes(n_atoms: int, lat: Lattice) -> int:
+    """Bytes of the optional workspace of the split direct sum (0: not used)."""
+    return int(library().cpmap_direct_workspace_bytes(int(n_atoms), int(lat.nx), int(lat.ny),
+                                                      int(lat.nz)))
+
+
+def direct_plan(n_atoms: int, lat: Lattice, with_workspace: bool = True):
+    """(cx, cy, cz, waves per workgroup, atom parts) of a direct launch."""
+    out = (_i32 * 5)()
+    _check("cpmap_direct_plan", library().cpmap_direct_plan(
+        int(n_atoms), int(lat.nx), int(lat.ny), int(lat.nz), int(bool(with_workspace)), out))
+    return tuple(out)
+
+
+def direct(atoms, lat: Lattice, out=None, split: bool = True, workspace=None):
+    """Direct Coulomb sum at every node; returns V with shape (nz, ny, nx) (x fastest).
+
+    split=True uses cpmap_direct_with_workspace with a workspace of
+    direct_workspace_bytes() (allocated here unless given as a uint8 GPU
+    tensor); split=False calls cpmap_direct.
+    """
     _check_atoms(atoms)
     V = _out(lat, atoms.device, out)
-    st = library().cpmap_direct(atoms.data_ptr() if atoms.numel() else None, atoms.shape[0],
-                                *_lat_args(lat), V.data_ptr() if V.numel() else None,
-                                _stream_ptr(atoms.device))
-    _check("cpmap_direct", st)
+    a_ptr = atoms.data_ptr() if atoms.numel() else None
+    v_ptr = V.data_ptr() if V.numel() else None
+    stream = _stream_ptr(atoms.device)
+    if not split:
+        st = library().cpmap_direct(a_ptr, atoms.shape[0], *_lat_args(lat), v_ptr, stream)
+        _check("cpmap_direct", st)
+        return V
+    need = direct_workspace_bytes(atoms.shape[0], lat)
+    if workspace is None and need > 0:
+        torch = _torch()
+        workspace = torch.empty(need, dtype=torch.uint8, device=atoms.device)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        torch = _torch()
+        if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 GPU tensor")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
+    st = library().cpmap_direct_with_workspace(a_ptr, atoms.shape[0], *_lat_args(lat), v_ptr,
+                                               ws_ptr, ws_bytes, stream)
+    _check("cpmap_direct_with_workspace", st)
     return V
 
 

@@ -169,9 +169,65 @@ cpmap_status cpmap_direct(const float *atoms, int64_t n_atoms, int32_t nx, int32
     if (!aligned(V, 4) || (atoms && !aligned(atoms, 16)))
         return CPMAP_EINVAL;
     hipError_t e = launch_direct(reinterpret_cast<const float4 *>(atoms), n_atoms, lat, V,
+                                 nullptr, 0, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? CPMAP_OK : CPMAP_EHIP;
+}
+
+size_t cpmap_direct_workspace_bytes(int64_t n_atoms, int32_t nx, int32_t ny, int32_t nz)
+{
+    if (n_atoms < 0 || n_atoms > CPMAP_MAX_ATOMS)
+        return 0;
+    if (check_lattice(nx, ny, nz, 1.0f, 0.0f, 0.0f, 0.0f) != CPMAP_OK)
+        return 0;
+    return direct_workspace_bytes(n_atoms, make_lattice(nx, ny, nz, 1.0f, 0.0f, 0.0f, 0.0f));
+}
+
+cpmap_status cpmap_direct_with_workspace(const float *atoms, int64_t n_atoms, int32_t nx,
+                                         int32_t ny, int32_t nz, float spacing, float ox,
+                                         float oy, float oz, float *V, void *workspace,
+                                         size_t workspace_bytes, void *stream)
+{
+    if (n_atoms < 0)
+        return CPMAP_EINVAL;
+    if (n_atoms > CPMAP_MAX_ATOMS)
+        return CPMAP_ERANGE;
+    cpmap_status st = check_lattice(nx, ny, nz, spacing, ox, oy, oz);
+    if (st != CPMAP_OK)
+        return st;
+    const Lattice lat = make_lattice(nx, ny, nz, spacing, ox, oy, oz);
+    if (lat.points() == 0)
+        return CPMAP_OK;
+    if (V == nullptr || (n_atoms > 0 && atoms == nullptr))
+        return CPMAP_EINVAL;
+    if (!aligned(V, 4) || (atoms && !aligned(atoms, 16)))
+        return CPMAP_EINVAL;
+    const size_t need = direct_workspace_bytes(n_atoms, lat);
+    if (need > 0 && (workspace == nullptr || !aligned(workspace, 256)))
+        return CPMAP_EINVAL;
+    if (workspace_bytes < need)
+        return CPMAP_ENOSPC;
+    hipError_t e = launch_direct(reinterpret_cast<const float4 *>(atoms), n_atoms, lat, V,
+                                 need > 0 ? workspace : nullptr, workspace_bytes,
                                  static_cast<hipStream_t>(stream));
     return e == hipSuccess ? CPMAP_OK : CPMAP_EHIP;
 }
+
+cpmap_status cpmap_direct_plan(int64_t n_atoms, int32_t nx, int32_t ny, int32_t nz,
+                               int32_t with_workspace, int32_t *plan_out)
+{
+    if (plan_out == nullptr || n_atoms < 0)
+        return CPMAP_EINVAL;
+    if (n_atoms > CPMAP_MAX_ATOMS)
+        return CPMAP_ERANGE;
+    cpmap_status st = check_lattice(nx, ny, nz, 1.0f, 0.0f, 0.0f, 0.0f);
+    if (st != CPMAP_OK)
+        return st;
+    direct_plan(n_atoms, make_lattice(nx, ny, nz, 1.0f, 0.0f, 0.0f, 0.0f), with_workspace != 0,
+                plan_out);
+    return CPMAP_OK;
+}
+
+int32_t cpmap_direct_occupancy_check(void) { return direct_occupancy_mismatches(); }
 
 cpmap_status cpmap_bin_grid(int32_t nx, int32_t ny, int32_t nz, float spacing, float ox, float oy,
                             float oz, float bin_size, float cutoff, int32_t *dims_out)

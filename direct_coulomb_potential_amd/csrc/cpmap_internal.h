@@ -53,8 +53,15 @@ struct Lattice {
     int64_t points() const { return (int64_t)n[0] * n[1] * n[2]; }
 };
 
+// Direct sum.  With a workspace of at least direct_workspace_bytes() the atoms
+// may also be split across workgroups into partial maps kept there.
 hipError_t launch_direct(const float4 *atoms, int64_t n_atoms, const Lattice &lat, float *V,
-                         hipStream_t stream);
+                         void *workspace, size_t workspace_bytes, hipStream_t stream);
+size_t direct_workspace_bytes(int64_t n_atoms, const Lattice &lat);
+// Blocking (cx, cy, cz), waves per workgroup and atom parts the launch uses.
+void direct_plan(int64_t n_atoms, const Lattice &lat, bool with_workspace, int32_t out[5]);
+// Variants whose runtime occupancy differs from the planning table.
+int direct_occupancy_mismatches();
 
 // Workspace layout of the binned atoms.
 struct BinLayout {

@@ -21,6 +21,13 @@
 //    a running total kept in LDS.  The short register sums bound fp32
 //    rounding growth for large same-sign atom sets, the fixed order keeps the
 //    result deterministic, and W fills the 1024 SIMDs for small lattices.
+//  - with a caller-provided workspace the atom list is also split into K
+//    contiguous parts across workgroups: each (part, node group) workgroup
+//    writes a partial map, and a second kernel adds the K maps in part order.
+//    The extra workgroups even out the last round of the 1024 SIMDs (977
+//    groups of 64 lanes x 128 nodes on a 200^3 lattice leave 5% of it idle)
+//    and keep the atom slices that run together small enough to share the
+//    scalar and L2 caches; the result stays deterministic.
 //  - nodes are stored x-fastest, V[(k*ny + j)*nx + i] (section 18.4) from the
 //    LDS total; lanes adjacent in x write adjacent 4*CX-byte runs.
 #include <algorithm>
@@ -64,11 +71,14 @@ __device__ __forceinline__ void accumulate_atom(const float4 a, const float (&x)
     }
 }
 
+// Workgroup b handles node group b % n_groups against atom part b / n_groups
+// and writes its nodes into out + part * part_stride (V itself when there is
+// one part, else the part's partial map in the workspace).
 template <int CX, int CY, int CZ, int W>
 __global__ __launch_bounds__(kWave *W) void direct_kernel(
     const float4 *__restrict__ atoms, int64_t n_atoms, int32_t nx, int32_t ny, int32_t nz,
-    int32_t nsx, int32_t nsy, int64_t n_strips, float h, float ox, float oy, float oz,
-    float *__restrict__ V)
+    int32_t nsx, int32_t nsy, int64_t n_strips, int64_t n_groups, int32_t n_parts,
+    int64_t part_stride, float h, float ox, float oy, float oz, float *__restrict__ out_base)
 {
     constexpr int NP = CX * CY * CZ;
     __shared__ float total[NP * kWave];
@@ -78,7 +88,10 @@ __global__ __launch_bounds__(kWave *W) void direct_kernel(
 
     // Lane -> block of nodes.  Lanes past the last block recompute the last
     // block (they still take part in the reduction) and store nothing.
-    const int64_t s_raw = (int64_t)blockIdx.x * kWave + lane;
+    const int64_t group = (int64_t)blockIdx.x % n_groups;
+    const int32_t part = (int32_t)((int64_t)blockIdx.x / n_groups);
+    float *__restrict__ V = out_base + (int64_t)part * part_stride;
+    const int64_t s_raw = group * kWave + lane;
     const bool live = s_raw < n_strips;
     const int64_t s = live ? s_raw : n_strips - 1;
     const int32_t sx = (int32_t)(s % nsx);
@@ -104,11 +117,13 @@ __global__ __launch_bounds__(kWave *W) void direct_kernel(
             total[p * kWave + lane] = 0.0f;
     }
 
-    // This wave's contiguous slice of the atoms, processed in rounds of at
-    // most kChunk atoms; every wave runs the same number of rounds.
-    const int64_t a_begin = n_atoms * slice / W;
-    const int64_t a_end = n_atoms * (slice + 1) / W;
-    const int64_t max_len = (n_atoms + W - 1) / W;
+    // This wave's contiguous slice of the part's atoms, processed in rounds
+    // of at most kChunk atoms; every wave runs the same number of rounds.
+    const int64_t p_begin = n_atoms * part / n_parts;
+    const int64_t p_len = n_atoms * (part + 1) / n_parts - p_begin;
+    const int64_t a_begin = p_begin + p_len * slice / W;
+    const int64_t a_end = p_begin + p_len * (slice + 1) / W;
+    const int64_t max_len = (p_len + W - 1) / W;
     const int64_t rounds = (max_len + kChunk - 1) / kChunk;
 
     for (int64_t r = 0; r < rounds; ++r) {
@@ -168,85 +183,139 @@ __global__ void fill_zero(float *__restrict__ V, int64_t n)
         V[i] = 0.0f;
 }
 
+// V[i] = sum over parts k = 0, 1, ... of part[k * n + i], in that order.
+__global__ void sum_parts(const float *__restrict__ parts, int32_t n_parts, int64_t n,
+                          float *__restrict__ V)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        float v = parts[i];
+        for (int32_t k = 1; k < n_parts; ++k)
+            v += parts[(int64_t)k * n + i];
+        V[i] = v;
+    }
+}
+
 using KernelFn = void (*)(const float4 *, int64_t, int32_t, int32_t, int32_t, int32_t, int32_t,
-                          int64_t, float, float, float, float, float *);
+                          int64_t, int64_t, int32_t, int64_t, float, float, float, float, float *);
 
 struct Variant {
     int cx, cy, cz, w;
+    int occupancy;  // waves per SIMD the compiled kernel allows (registers, LDS)
     KernelFn kernel;
 };
 
-#define CPMAP_VARIANT(CX, CY, CZ, W) Variant{CX, CY, CZ, W, direct_kernel<CX, CY, CZ, W>}
+#define CPMAP_VARIANT(CX, CY, CZ, W, OCC) Variant{CX, CY, CZ, W, OCC, direct_kernel<CX, CY, CZ, W>}
 
+// Occupancies are those of the gfx950 build (189, 117, 69, 54, 41 and 29
+// VGPRs; LDS never limits); a GPU test checks them against the runtime.
 const Variant kVariants[] = {
-    CPMAP_VARIANT(8, 8, 2, 4),  CPMAP_VARIANT(8, 8, 2, 8),  CPMAP_VARIANT(8, 4, 2, 4),
-    CPMAP_VARIANT(8, 4, 2, 8),  CPMAP_VARIANT(4, 4, 2, 8),  CPMAP_VARIANT(4, 4, 2, 16),
-    CPMAP_VARIANT(4, 4, 1, 16), CPMAP_VARIANT(2, 2, 1, 16), CPMAP_VARIANT(1, 1, 1, 16),
+    CPMAP_VARIANT(8, 8, 2, 4, 2),  CPMAP_VARIANT(8, 8, 2, 8, 2),  CPMAP_VARIANT(8, 4, 2, 4, 4),
+    CPMAP_VARIANT(8, 4, 2, 8, 4),  CPMAP_VARIANT(4, 4, 2, 8, 6),  CPMAP_VARIANT(4, 4, 2, 16, 4),
+    CPMAP_VARIANT(4, 4, 1, 16, 8), CPMAP_VARIANT(2, 2, 1, 16, 8), CPMAP_VARIANT(1, 1, 1, 16, 8),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
+constexpr int kMaxParts = 32;
+constexpr double kMaxPartBytes = 1u << 30;  // cap on the partial maps of one call
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Waves of one variant that a SIMD holds at once, from the runtime's
-// occupancy calculator (registers and LDS of the compiled kernel); cached.
-int waves_per_simd(int idx)
-{
-    static std::atomic<int> cache[kNumVariants];
-    int v = cache[idx].load(std::memory_order_relaxed);
-    if (v > 0)
-        return v;
-    const Variant &var = kVariants[idx];
-    int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, var.kernel, kWave * var.w, 0) !=
-            hipSuccess ||
-        blocks <= 0)
-        blocks = 1;
-    v = std::max(1, blocks * var.w / 4);
-    cache[idx].store(v, std::memory_order_relaxed);
-    return v;
-}
+struct Plan {
+    int variant;
+    int32_t parts;
+    double seconds;
+};
 
-// Modelled run time of a variant, in VALU issue slots of the busiest SIMD.
-//  - a pair costs 4 slots (fma, half-rate v_rsq_f32, fma) plus the blocking's
-//    shared per-atom work;
-//  - workgroups spread evenly over the 256 CUs and each puts W/4 waves on
-//    every SIMD of its CU; a SIMD runs `occ` waves at once, and needs two
-//    resident waves to keep its VALU busy, so a lone wave runs at half rate.
-double variant_cost(int idx, const Lattice &lat, int64_t n_atoms)
+// Modelled run time of a variant with the atoms split into `parts` across
+// workgroups:
+//  - a pair costs 4 VALU issue slots (fma, half-rate v_rsq_f32, fma) plus the
+//    blocking's shared per-atom work;
+//  - workgroups spread evenly over the 256 CUs, each putting W/4 waves on
+//    every SIMD of its CU; a SIMD runs `occupancy` waves at once and needs two
+//    resident waves to keep its VALU busy, so a lone wave runs at half rate;
+//  - one issue slot of a wave is 4 cycles at 2.4 GHz;
+//  - with parts > 1, the partial maps are written once and summed once.
+double plan_seconds(const Variant &v, int32_t parts, const Lattice &lat, int64_t n_atoms)
 {
-    const Variant &v = kVariants[idx];
     const int64_t strips = ceil_div(lat.n[0], v.cx) * ceil_div(lat.n[1], v.cy) *
                            ceil_div(lat.n[2], v.cz);
     const int64_t groups = ceil_div(strips, kWave);
     const double np = v.cx * v.cy * v.cz;
     const double per_pair = 4.0 + (v.cx + v.cy + 2.0 * v.cz + v.cy * v.cz) / np;
-    const double wave_work = std::ceil((double)n_atoms / v.w) * np * per_pair + 64.0 * np;
-    const int64_t per_simd = ceil_div(groups, 256) * std::max(1, v.w / 4);
-    const int occ = waves_per_simd(idx);
+    const double atoms_per_wave = std::ceil((double)n_atoms / ((double)parts * v.w));
+    const double wave_work = atoms_per_wave * np * per_pair + 2000.0 + 64.0 * np;
+    const int per_wg = std::max(1, v.w / 4);
+    const int64_t per_simd = ceil_div(groups * parts, 256) * per_wg;
+    const int occ = std::max(per_wg, v.occupancy / per_wg * per_wg);
     double units = 0.0;
     for (int64_t left = per_simd; left > 0; left -= occ)
         units += (double)std::max<int64_t>(std::min<int64_t>(left, occ), 2);
-    return units * wave_work;
+    double t = units * wave_work * 4.0 / 2.4e9;
+    if (parts > 1)
+        t += (2.0 * parts + 1.0) * 4.0 * (double)lat.points() / 4.0e12 + 5e-6;
+    return t;
 }
 
-const Variant &pick_variant(const Lattice &lat, int64_t n_atoms)
+Plan make_plan(const Lattice &lat, int64_t n_atoms, bool allow_parts)
 {
-    int best = 0;
-    double best_cost = variant_cost(0, lat, n_atoms);
-    for (int i = 1; i < kNumVariants; ++i) {
-        const double c = variant_cost(i, lat, n_atoms);
-        if (c < best_cost) {
-            best_cost = c;
-            best = i;
+    Plan best{0, 1, plan_seconds(kVariants[0], 1, lat, n_atoms)};
+    const int max_parts = allow_parts ? kMaxParts : 1;
+    for (int i = 0; i < kNumVariants; ++i) {
+        for (int32_t k = 1; k <= max_parts; ++k) {
+            if (k > 1 && (double)k * 4.0 * (double)lat.points() > kMaxPartBytes)
+                break;
+            if (k > 1 && n_atoms < (int64_t)k * kVariants[i].w * 64)
+                break;  // keep at least 64 atoms per wave
+            const double t = plan_seconds(kVariants[i], k, lat, n_atoms);
+            // prefer fewer parts (less workspace) unless clearly faster
+            if (t < best.seconds * (k > best.parts ? 0.995 : 1.0)) {
+                best = Plan{i, k, t};
+            }
         }
     }
-    return kVariants[best];
+    return best;
+}
+
+size_t plan_workspace(const Plan &p, const Lattice &lat)
+{
+    return p.parts > 1 ? (size_t)p.parts * (size_t)lat.points() * sizeof(float) : 0;
 }
 
 }  // namespace
 
+size_t direct_workspace_bytes(int64_t n_atoms, const Lattice &lat)
+{
+    if (lat.points() == 0 || n_atoms == 0)
+        return 0;
+    return plan_workspace(make_plan(lat, n_atoms, true), lat);
+}
+
+void direct_plan(int64_t n_atoms, const Lattice &lat, bool with_workspace, int32_t out[5])
+{
+    const Plan p = make_plan(lat, n_atoms, with_workspace);
+    const Variant &v = kVariants[p.variant];
+    out[0] = v.cx;
+    out[1] = v.cy;
+    out[2] = v.cz;
+    out[3] = v.w;
+    out[4] = p.parts;
+}
+
+int direct_occupancy_mismatches()
+{
+    int bad = 0;
+    for (const Variant &v : kVariants) {
+        int blocks = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, v.kernel, kWave * v.w, 0) !=
+                hipSuccess ||
+            blocks * v.w / 4 != v.occupancy)
+            ++bad;
+    }
+    return bad;
+}
+
 hipError_t launch_direct(const float4 *atoms, int64_t n_atoms, const Lattice &lat, float *V,
-                         hipStream_t stream)
+                         void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
     const int64_t points = lat.points();
     if (points == 0)
@@ -256,15 +325,24 @@ hipError_t launch_direct(const float4 *atoms, int64_t n_atoms, const Lattice &la
         hipLaunchKernelGGL(fill_zero, dim3((unsigned)blocks), dim3(256), 0, stream, V, points);
         return hipGetLastError();
     }
-    const Variant &v = pick_variant(lat, n_atoms);
+    Plan plan = make_plan(lat, n_atoms, workspace != nullptr);
+    if (plan_workspace(plan, lat) > workspace_bytes)
+        plan = make_plan(lat, n_atoms, false);
+    const Variant &v = kVariants[plan.variant];
     const int32_t nsx = (int32_t)ceil_div(lat.n[0], v.cx);
     const int32_t nsy = (int32_t)ceil_div(lat.n[1], v.cy);
     const int64_t nsz = ceil_div(lat.n[2], v.cz);
     const int64_t strips = (int64_t)nsx * nsy * nsz;
-    const int64_t blocks = ceil_div(strips, kWave);
-    hipLaunchKernelGGL(v.kernel, dim3((unsigned)blocks), dim3(kWave * v.w), 0, stream, atoms,
-                       n_atoms, lat.n[0], lat.n[1], lat.n[2], nsx, nsy, strips, lat.h, lat.o[0],
-                       lat.o[1], lat.o[2], V);
+    const int64_t groups = ceil_div(strips, kWave);
+    float *out = plan.parts > 1 ? static_cast<float *>(workspace) : V;
+    hipLaunchKernelGGL(v.kernel, dim3((unsigned)(groups * plan.parts)), dim3(kWave * v.w), 0,
+                       stream, atoms, n_atoms, lat.n[0], lat.n[1], lat.n[2], nsx, nsy, strips,
+                       groups, plan.parts, points, lat.h, lat.o[0], lat.o[1], lat.o[2], out);
+    if (plan.parts > 1) {
+        const int64_t blocks = std::min<int64_t>(ceil_div(points, 256), 8192);
+        hipLaunchKernelGGL(sum_parts, dim3((unsigned)blocks), dim3(256), 0, stream, out,
+                           plan.parts, points, V);
+    }
     return hipGetLastError();
 }
 

@@ -85,6 +85,53 @@ cpmap_status cpmap_direct(const float *atoms, int64_t n_atoms,
                           float *V, void *stream);
 
 /*
+ * cpmap_direct_workspace_bytes -- size of the optional workspace that lets
+ * cpmap_direct_with_workspace split the atom list across workgroups (0 when
+ * the lattice and atom count gain nothing from it).  Host only, no HIP call;
+ * depends only on n_atoms and the lattice dimensions.  0 on invalid input.
+ */
+size_t cpmap_direct_workspace_bytes(int64_t n_atoms, int32_t nx, int32_t ny, int32_t nz);
+
+/*
+ * cpmap_direct_with_workspace -- the same direct sum as cpmap_direct, with a
+ * caller-owned scratch buffer.  The library may then also split the atoms
+ * into K contiguous parts handled by different workgroups, write K partial
+ * maps into the workspace and add them in part order (still no atomics,
+ * still deterministic); on large lattices this evens out the last round of
+ * workgroups over the GPU.  Results agree with cpmap_direct within the
+ * accuracy bound (the summation order differs).
+ *
+ *   workspace        device, >= cpmap_direct_workspace_bytes(...) bytes,
+ *                    256-byte aligned (may be NULL when that size is 0);
+ *                    overwritten, must stay valid until the work completes
+ *   workspace_bytes  its size; CPMAP_ENOSPC when too small
+ * Other arguments, ownership and errors as cpmap_direct.
+ */
+cpmap_status cpmap_direct_with_workspace(const float *atoms, int64_t n_atoms,
+                                         int32_t nx, int32_t ny, int32_t nz, float spacing,
+                                         float ox, float oy, float oz, float *V,
+                                         void *workspace, size_t workspace_bytes,
+                                         void *stream);
+
+/*
+ * cpmap_direct_plan -- how a direct call of this size is launched: plan_out
+ * (host, 5 int32) receives nodes per lane along x, y, z, waves per
+ * workgroup, and atom parts across workgroups.  with_workspace selects the
+ * plan of cpmap_direct_with_workspace (nonzero) or of cpmap_direct (0).
+ * Host only, no HIP call.
+ */
+cpmap_status cpmap_direct_plan(int64_t n_atoms, int32_t nx, int32_t ny, int32_t nz,
+                               int32_t with_workspace, int32_t *plan_out);
+
+/*
+ * cpmap_direct_occupancy_check -- number of compiled direct-kernel variants
+ * whose occupancy on the current device differs from the table the planner
+ * assumes (0 when they all agree).  Calls the HIP runtime's occupancy query
+ * (no device work).  A mismatch affects speed, never results.
+ */
+int32_t cpmap_direct_occupancy_check(void);
+
+/*
  * Bin geometry (shared by the three cutoff calls below).  With bin size bs
  * and cutoff rc: halo H = ceil(rc/bs) bins on every side of the lattice; bin
  * grid origin b0 = fl(o - H*bs) per axis; nb per axis = floor(t_last) + 1 + H

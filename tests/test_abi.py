@@ -119,3 +119,25 @@ def test_binding_rejects_cpu_and_wrong_dtype_tensors():
         cpmap.direct(torch.zeros(4, 3, dtype=torch.float32), Lattice(2, 2, 2, 0.5))
     with pytest.raises(TypeError):
         cpmap.direct([[0, 0, 0, 1]], Lattice(2, 2, 2, 0.5))
+
+
+def test_direct_workspace_queries_and_checks():
+    lib = cpmap.library()
+    need = lib.cpmap_direct_workspace_bytes(200_000, 200, 200, 200)
+    assert need > 0 and need % (4 * 200**3) == 0
+    assert lib.cpmap_direct_workspace_bytes(-1, 200, 200, 200) == 0
+    assert lib.cpmap_direct_workspace_bytes(10, -1, 2, 2) == 0
+    assert cpmap.direct_plan(200_000, Lattice(200, 200, 200, 0.5), True)[4] == need // (4 * 200**3)
+    assert cpmap.direct_plan(200_000, Lattice(200, 200, 200, 0.5), False)[4] == 1
+    assert cpmap.direct_plan(1, Lattice(1, 1, 1, 0.5), True)[4] == 1
+    assert lib.cpmap_direct_workspace_bytes(1, 1, 1, 1) == 0
+    ws = ctypes.c_void_p(0x100000)
+    args = (FAKE, 200_000, 200, 200, 200, 0.5, 0.0, 0.0, 0.0, FAKE)
+    assert lib.cpmap_direct_with_workspace(*args, ws, need - 1, None) == ENOSPC
+    assert lib.cpmap_direct_with_workspace(*args, None, need, None) == EINVAL
+    assert lib.cpmap_direct_with_workspace(*args, ctypes.c_void_p(0x100010), need, None) == EINVAL
+    assert lib.cpmap_direct_with_workspace(FAKE, -1, 200, 200, 200, 0.5, 0.0, 0.0, 0.0, FAKE, ws, need, None) == EINVAL
+    assert lib.cpmap_direct_with_workspace(FAKE, 10, 0, 200, 200, 0.5, 0.0, 0.0, 0.0, None, None, 0, None) == OK
+    out = (ctypes.c_int32 * 5)()
+    assert lib.cpmap_direct_plan(10, 2, 2, 2, 1, None) == EINVAL
+    assert lib.cpmap_direct_plan(-1, 2, 2, 2, 1, out) == EINVAL

@@ -26,9 +26,9 @@ def torch():
     return torch
 
 
-def _run_direct(torch, atoms_np, lat):
+def _run_direct(torch, atoms_np, lat, split=True):
     atoms = torch.from_numpy(np.ascontiguousarray(atoms_np, dtype=np.float32)).cuda()
-    V = cpmap.direct(atoms, lat)
+    V = cpmap.direct(atoms, lat, split=split)
     torch.cuda.synchronize()
     return V.cpu().numpy().reshape(-1)
 
@@ -57,13 +57,15 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("split", [False, True], ids=["plain", "split"])
 @pytest.mark.parametrize("case", CASES, ids=[f"n{c[0]}_{c[1][0]}x{c[1][1]}x{c[1][2]}" for c in CASES])
-def test_direct_small_all_nodes(torch, case):
+def test_direct_small_all_nodes(torch, case, split):
     n, dims, h, origin, lo, hi, seed = case
     atoms = wl.random_atoms(n, lo, hi, seed=seed)
     lat = Lattice(*dims, h, origin)
-    print(f"[direct] n={n} dims={dims} h={h} origin={origin}", flush=True)
-    Vg = _run_direct(torch, atoms, lat)
+    print(f"[direct] n={n} dims={dims} h={h} origin={origin} plan={cpmap.direct_plan(n, lat, split)}",
+          flush=True)
+    Vg = _run_direct(torch, atoms, lat, split)
     Vo, S = oracle.direct(atoms, dims, h, origin, with_scale=True)
     _assert_parity(Vg, Vo, S, f"n={n} dims={dims}")
 
@@ -90,24 +92,50 @@ def test_direct_zero_charges_and_far_atoms(torch):
     _assert_parity(Vg2, Vo2, S, "zero charges removed")
 
 
-def test_direct_same_sign_charges_large_n(torch):
+@pytest.mark.parametrize("split", [False, True], ids=["plain", "split"])
+def test_direct_same_sign_charges_large_n(torch, split):
     """All-positive charges over many atoms: the blocked fp32 sum must stay
     inside the bound even though no cancellation hides rounding."""
     atoms = wl.random_atoms(200_000, (0, 0, 0), (20, 20, 20), seed=10, q_lo=0.0, q_hi=1.0)
     lat = Lattice(16, 12, 10, 1.25, (0.1, 0.2, 0.3))
-    Vg = _run_direct(torch, atoms, lat)
+    Vg = _run_direct(torch, atoms, lat, split)
     Vo, S = oracle.direct(atoms, lat.dims, lat.spacing, lat.origin, with_scale=True)
     worst = _assert_parity(Vg, Vo, S, "same sign")
     print(f"same-sign worst |err|/S = {worst:.3e}")
 
 
-def test_direct_is_deterministic(torch):
-    atoms = torch.from_numpy(wl.random_atoms(5000, (0, 0, 0), (10, 10, 10), seed=12)).cuda()
-    lat = Lattice(40, 30, 20, 0.25)
-    a = cpmap.direct(atoms, lat).clone()
-    b = cpmap.direct(atoms, lat)
+@pytest.mark.parametrize("split", [False, True], ids=["plain", "split"])
+def test_direct_is_deterministic(torch, split):
+    atoms = torch.from_numpy(wl.random_atoms(50_000, (0, 0, 0), (20, 20, 20), seed=12)).cuda()
+    lat = Lattice(80, 60, 40, 0.25)
+    a = cpmap.direct(atoms, lat, split=split).clone()
+    b = cpmap.direct(atoms, lat, split=split)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_direct_planner_occupancy_table_matches_device(torch):
+    """The planner's per-variant occupancy table equals what the runtime
+    reports for the compiled kernels (a mismatch would only cost speed)."""
+    assert cpmap.library().cpmap_direct_occupancy_check() == 0
+
+
+def test_direct_split_workspace_is_used_and_reusable(torch):
+    """A caller-provided workspace is accepted, reused across calls of the
+    same size, and a too-small one is refused."""
+    w = wl.full_direct()
+    lat = w.lattice
+    need = cpmap.direct_workspace_bytes(w.n_atoms, lat)
+    assert need > 0
+    atoms = torch.from_numpy(w.atoms).cuda()
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    a = cpmap.direct(atoms, lat, workspace=ws).clone()
+    b = cpmap.direct(atoms, lat, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    with pytest.raises(cpmap.CpmapError) as e:
+        cpmap.direct(atoms, lat, workspace=ws[: need - 256])
+    assert e.value.status == 3
 
 
 def test_direct_rejects_unbinned_geometry_errors(torch):
@@ -118,23 +146,25 @@ def test_direct_rejects_unbinned_geometry_errors(torch):
         cpmap.direct(atoms, Lattice(2, 2, 2, 0.0))
 
 
+@pytest.mark.parametrize("split", [False, True], ids=["plain", "split"])
 @pytest.mark.parametrize("index", [1, 2])
-def test_direct_workload_all_nodes(torch, index):
+def test_direct_workload_all_nodes(torch, index, split):
     w = wl.workload(index)
     lat = w.lattice
-    print(f"[direct] workload {w.name}", flush=True)
-    Vg = _run_direct(torch, w.atoms, lat)
+    print(f"[direct] workload {w.name} plan={cpmap.direct_plan(w.n_atoms, lat, split)}", flush=True)
+    Vg = _run_direct(torch, w.atoms, lat, split)
     Vo, S = oracle.direct(w.atoms, lat.dims, lat.spacing, lat.origin, with_scale=True)
     worst = _assert_parity(Vg, Vo, S, w.name)
     print(f"{w.name}: worst |err|/S = {worst:.3e}")
 
 
+@pytest.mark.parametrize("split", [False, True], ids=["plain", "split"])
 @pytest.mark.parametrize("index", [3, 4])
-def test_direct_workload_checked_nodes(torch, index):
+def test_direct_workload_checked_nodes(torch, index, split):
     w = wl.workload(index)
     lat = w.lattice
-    print(f"[direct] workload {w.name}", flush=True)
-    Vg = _run_direct(torch, w.atoms, lat)
+    print(f"[direct] workload {w.name} plan={cpmap.direct_plan(w.n_atoms, lat, split)}", flush=True)
+    Vg = _run_direct(torch, w.atoms, lat, split)
     nodes = wl.checked_nodes(lat)
     Vo, S = oracle.direct(w.atoms, lat.dims, lat.spacing, lat.origin, nodes=nodes, with_scale=True)
     worst = _assert_parity(Vg[nodes], Vo, S, w.name)
