@@ -243,16 +243,16 @@ double plan_seconds(const Variant &v, int32_t parts, const Lattice &lat, int64_t
     const double np = v.cx * v.cy * v.cz;
     const double per_pair = 4.0 + (v.cx + v.cy + 2.0 * v.cz + v.cy * v.cz) / np;
     const double atoms_per_wave = std::ceil((double)n_atoms / ((double)parts * v.w));
-    const double wave_work = atoms_per_wave * np * per_pair + 2000.0 + 64.0 * np;
+    const double wave_work = atoms_per_wave * np * per_pair + 500.0;
     const int per_wg = std::max(1, v.w / 4);
     const int64_t per_simd = ceil_div(groups * parts, 256) * per_wg;
     const int occ = std::max(per_wg, v.occupancy / per_wg * per_wg);
     double units = 0.0;
     for (int64_t left = per_simd; left > 0; left -= occ)
-        units += (double)std::max<int64_t>(std::min<int64_t>(left, occ), 2);
+        units += std::max((double)std::min<int64_t>(left, occ), 1.5);
     double t = units * wave_work * 4.0 / 2.4e9;
     if (parts > 1)
-        t += (2.0 * parts + 1.0) * 4.0 * (double)lat.points() / 4.0e12 + 5e-6;
+        t += (2.0 * parts + 1.0) * 4.0 * (double)lat.points() / 8.0e12 + 3e-6;
     return t;
 }
 
