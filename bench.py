@@ -220,6 +220,9 @@ def bench_cutoff(torch, cpmap, wl, dev, args):
     def run_cut():
         cpmap.cutoff(ws, w.n_atoms, lat, bs, rc, out=V)
 
+    def run_trunc():
+        cpmap.cutoff(ws, w.n_atoms, lat, bs, rc, out=V, term="truncated")
+
     def run_both():
         flush.zero_()
         run_bin()
@@ -228,6 +231,7 @@ def bench_cutoff(torch, cpmap, wl, dev, args):
     steps = max(args.steps, 5)
     _, per_bin = time_launches(torch, run_bin, steps, args.warmup)
     _, per_cut = time_launches(torch, run_cut, steps, args.warmup)
+    _, per_trunc = time_launches(torch, run_trunc, steps, args.warmup)
     wall_e2e, _ = time_launches(torch, run_both, steps, args.warmup)
     cut_ms = statistics.median(per_cut)
     bin_ms = statistics.median(per_bin)
@@ -246,6 +250,7 @@ def bench_cutoff(torch, cpmap, wl, dev, args):
         "bin_ms_median": bin_ms,
         "cutoff_ms_median": cut_ms,
         "cutoff_ms_min": min(per_cut),
+        "truncated_term_ms_median": statistics.median(per_trunc),
         "end_to_end_ms_with_l2_flush": wall_e2e / steps * 1e3,
         "direct_same_atoms_ms": dir_ms,
         "speedup_vs_direct": dir_ms / (cut_ms + bin_ms),

@@ -61,6 +61,7 @@ _SIGNATURES = {
     "cpmap_workspace_layout": (_i32, [_i64, *_LAT, _f32, _f32, ctypes.POINTER(_i64),
                                       ctypes.POINTER(_i64)]),
     "cpmap_cutoff": (_i32, [_vp, _sz, _i64, *_LAT, _f32, _f32, _vp, _vp]),
+    "cpmap_cutoff_term": (_i32, [_vp, _sz, _i64, *_LAT, _f32, _f32, _i32, _vp, _vp]),
     "cpmap_neighbor_spans": (_i64, [*_LAT, _f32, _f32, _i32, _i32, _i32, ctypes.POINTER(_i32),
                                     _i64]),
 }
@@ -238,13 +239,23 @@ def workspace_views(workspace, n_atoms: int, lat: Lattice, bin_size: float, cuto
     return starts, srt
 
 
-def cutoff(workspace, n_atoms: int, lat: Lattice, bin_size: float, cutoff: float, out=None):
-    """Smoothed short-range potential with cutoff binning; returns V (nz, ny, nx)."""
+TERMS = {"smoothed": 0, "truncated": 1}
+
+
+def cutoff(workspace, n_atoms: int, lat: Lattice, bin_size: float, cutoff: float, out=None,
+           term: str = "smoothed"):
+    """Cutoff sum over binned atoms; returns V (nz, ny, nx).
+
+    term="smoothed": q (1/r - gamma(r^2)) (cpmap_cutoff); term="truncated": q/r
+    with the fp32 inclusion test of cpmap_cutoff_term.
+    """
+    if term not in TERMS:
+        raise ValueError(f"term must be one of {sorted(TERMS)}")
     V = _out(lat, workspace.device, out)
-    st = library().cpmap_cutoff(workspace.data_ptr(), workspace.numel(), int(n_atoms),
-                                *_lat_args(lat), float(bin_size), float(cutoff), V.data_ptr(),
-                                _stream_ptr(workspace.device))
-    _check("cpmap_cutoff", st)
+    st = library().cpmap_cutoff_term(workspace.data_ptr(), workspace.numel(), int(n_atoms),
+                                     *_lat_args(lat), float(bin_size), float(cutoff),
+                                     TERMS[term], V.data_ptr(), _stream_ptr(workspace.device))
+    _check("cpmap_cutoff_term", st)
     return V
 
 

@@ -312,14 +312,17 @@ cpmap_status cpmap_bin_atoms(const float *atoms, int64_t n_atoms, int32_t nx, in
     return CPMAP_OK;
 }
 
-cpmap_status cpmap_cutoff(const void *workspace, size_t workspace_bytes, int64_t n_atoms,
-                          int32_t nx, int32_t ny, int32_t nz, float spacing, float ox, float oy,
-                          float oz, float bin_size, float cutoff, float *V, void *stream)
+cpmap_status cpmap_cutoff_term(const void *workspace, size_t workspace_bytes, int64_t n_atoms,
+                               int32_t nx, int32_t ny, int32_t nz, float spacing, float ox,
+                               float oy, float oz, float bin_size, float cutoff, int32_t term,
+                               float *V, void *stream)
 {
     if (n_atoms < 0)
         return CPMAP_EINVAL;
     if (n_atoms > CPMAP_MAX_ATOMS)
         return CPMAP_ERANGE;
+    if (term != CPMAP_TERM_SMOOTHED && term != CPMAP_TERM_TRUNCATED)
+        return CPMAP_EINVAL;
     BinGeometry g;
     cpmap_status st = make_bin_geometry(nx, ny, nz, spacing, ox, oy, oz, bin_size, cutoff, &g);
     if (st != CPMAP_OK)
@@ -339,9 +342,17 @@ cpmap_status cpmap_cutoff(const void *workspace, size_t workspace_bytes, int64_t
             return CPMAP_EGEOM;
     }
     const Lattice lat = make_lattice(nx, ny, nz, spacing, ox, oy, oz);
-    hipError_t e = launch_cutoff(workspace, L, n_atoms, lat, g, V,
+    hipError_t e = launch_cutoff(workspace, L, n_atoms, lat, g, term, V,
                                  static_cast<hipStream_t>(stream));
     return e == hipSuccess ? CPMAP_OK : CPMAP_EHIP;
+}
+
+cpmap_status cpmap_cutoff(const void *workspace, size_t workspace_bytes, int64_t n_atoms,
+                          int32_t nx, int32_t ny, int32_t nz, float spacing, float ox, float oy,
+                          float oz, float bin_size, float cutoff, float *V, void *stream)
+{
+    return cpmap_cutoff_term(workspace, workspace_bytes, n_atoms, nx, ny, nz, spacing, ox, oy, oz,
+                             bin_size, cutoff, CPMAP_TERM_SMOOTHED, V, stream);
 }
 
 }  // extern "C"

@@ -83,7 +83,8 @@ hipError_t launch_bin_atoms(const float4 *atoms, int64_t n_atoms, const Lattice 
                             hipStream_t stream);
 
 hipError_t launch_cutoff(const void *workspace, const BinLayout &L, int64_t n_atoms,
-                         const Lattice &lat, const BinGeometry &g, float *V, hipStream_t stream);
+                         const Lattice &lat, const BinGeometry &g, int32_t term, float *V,
+                         hipStream_t stream);
 
 // Neighbourhood of one 8x8x8 tile as x-runs of bins; host and device.
 constexpr int kTile = 8;

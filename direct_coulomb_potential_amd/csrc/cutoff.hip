@@ -1,9 +1,12 @@
-// Smoothed short-range potential with cutoff binning on gfx950.
+// Cutoff summation with spatial bins on gfx950.
 //
-// For every node g: V(g) = sum over atoms with r^2 < rc^2 of
-//   q * (1/r - (GC0 + r^2 (GC1 + r^2 GC2)))
-// (the binning lecture's large-bin kernel slide gives the term; the constants
-// make it vanish with its first two derivatives at rc).
+// For every node g, over the atoms with r^2 < rc^2:
+//   smoothed   V(g) = sum q * (1/r - (GC0 + r^2 (GC1 + r^2 GC2)))
+//              (the binning lecture's large-bin kernel slide gives the term;
+//              the constants make it vanish with two derivatives at rc);
+//   truncated  V(g) = sum q / r  (the case-study notes' section 18.5 listing),
+//              with the inclusion test taken in fp32 as r^2 = fma(dx, dx,
+//              fma(dy, dy, dz*dz)) < fl(rc*rc).
 //
 // Structure (the lecture's small-bin design, re-planned for CDNA4):
 //  - one workgroup per 8x8x8 tile of nodes (4 A of lattice at 0.5 A spacing,
@@ -158,6 +161,8 @@ constexpr int kThreads = kTile * kTile * kTile / kNx;  // 128
 constexpr int kStage = 1024;                           // atoms staged per chunk (16 KB)
 constexpr int kMaxRows = 256;                          // (cy, cz) rows per list chunk
 
+enum TermMode { kSmoothClamp = 0, kSmoothSelect = 1, kTruncated = 2 };
+
 struct CutoffParams {
     float h, o[3];
     int32_t n[3];
@@ -165,16 +170,18 @@ struct CutoffParams {
     float b0[3];
     int32_t nb[3];
     float bs, rc, rc2;
+    float list_rc;  // radius of the bin neighbourhood (rc, widened for the truncated term)
     float gc0, gc1, gc2;
+    int32_t truncated;
 };
 
 constexpr int kWaves = kThreads / 64;
 
-// One staged atom against this lane's kNx nodes.  With kClamp, r^2 is
-// clamped to P.rc2, for which the kernel has checked that the fp32 term is
-// exactly 0 (so atoms beyond the cutoff add exactly nothing); otherwise the
-// charge is replaced by 0 outside the cutoff.
-template <bool kClamp>
+// One staged atom against this lane's kNx nodes.  kSmoothClamp clamps r^2 to
+// P.rc2, for which the kernel has checked that the fp32 smoothed term is
+// exactly 0 (so atoms beyond the cutoff add exactly nothing); kSmoothSelect
+// and kTruncated replace the charge by 0 outside the cutoff.
+template <int MODE>
 __device__ __forceinline__ void add_atom(const float4 at, const float (&x)[kNx], float y, float z,
                                          const CutoffParams &P, float (&acc)[kNx])
 {
@@ -184,17 +191,21 @@ __device__ __forceinline__ void add_atom(const float4 at, const float (&x)[kNx],
 #pragma unroll
     for (int c = 0; c < kNx; ++c) {
         const float dx = x[c] - at.x;
-        if constexpr (kClamp) {
+        if constexpr (MODE == kSmoothClamp) {
             const float r2 = fminf(fmaf(dx, dx, yz2), P.rc2);
             const float rs = __builtin_amdgcn_rsqf(r2);
             const float g = fmaf(fmaf(r2, P.gc2, P.gc1), r2, P.gc0);
             acc[c] = fmaf(at.w, rs - g, acc[c]);
-        } else {
+        } else if constexpr (MODE == kSmoothSelect) {
             const float r2 = fmaf(dx, dx, yz2);
             const float rs = __builtin_amdgcn_rsqf(r2);
             const float g = fmaf(fmaf(r2, P.gc2, P.gc1), r2, P.gc0);
             const float qm = r2 < P.rc2 ? at.w : 0.0f;
             acc[c] = fmaf(qm, rs - g, acc[c]);
+        } else {
+            const float r2 = fmaf(dx, dx, yz2);
+            const float qm = r2 < P.rc2 ? at.w : 0.0f;
+            acc[c] = fmaf(qm, __builtin_amdgcn_rsqf(r2), acc[c]);
         }
     }
 }
@@ -223,7 +234,7 @@ __device__ inline float exact_zero_clamp(const CutoffParams &P)
     return 0.0f;
 }
 
-template <bool kClamp>
+template <int MODE>
 __device__ __forceinline__ void sweep(const float4 *stage, const uint16_t *list, int32_t listed,
                                       const float (&x)[kNx], float y, float z,
                                       const CutoffParams &P, float (&acc)[kNx])
@@ -234,13 +245,13 @@ __device__ __forceinline__ void sweep(const float4 *stage, const uint16_t *list,
         const float4 a1 = stage[list[i + 1]];
         const float4 a2 = stage[list[i + 2]];
         const float4 a3 = stage[list[i + 3]];
-        add_atom<kClamp>(a0, x, y, z, P, acc);
-        add_atom<kClamp>(a1, x, y, z, P, acc);
-        add_atom<kClamp>(a2, x, y, z, P, acc);
-        add_atom<kClamp>(a3, x, y, z, P, acc);
+        add_atom<MODE>(a0, x, y, z, P, acc);
+        add_atom<MODE>(a1, x, y, z, P, acc);
+        add_atom<MODE>(a2, x, y, z, P, acc);
+        add_atom<MODE>(a3, x, y, z, P, acc);
     }
     for (; i < listed; ++i)
-        add_atom<kClamp>(stage[list[i]], x, y, z, P, acc);
+        add_atom<MODE>(stage[list[i]], x, y, z, P, acc);
 }
 
 __global__ __launch_bounds__(kThreads) void cutoff_kernel(CutoffParams P0,
@@ -254,13 +265,17 @@ __global__ __launch_bounds__(kThreads) void cutoff_kernel(CutoffParams P0,
     __shared__ int32_t span_off[kMaxRows + 1];
     __shared__ int32_t scan_tmp[kThreads];
 
-    // Clamp r^2 where a clamp value with an exactly-zero term exists.
+    // Smoothed term: clamp r^2 where a clamp value with an exactly-zero term
+    // exists, else select.  Truncated term: select.
     CutoffParams P = P0;
-    const float clamp =
-        __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(exact_zero_clamp(P0))));
-    const bool use_clamp = clamp > 0.0f;
-    if (use_clamp)
-        P.rc2 = clamp;
+    int mode = kTruncated;
+    if (!P0.truncated) {
+        const float clamp = __uint_as_float(
+            __builtin_amdgcn_readfirstlane(__float_as_uint(exact_zero_clamp(P0))));
+        mode = clamp > 0.0f ? kSmoothClamp : kSmoothSelect;
+        if (mode == kSmoothClamp)
+            P.rc2 = clamp;
+    }
 
     const int t = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(t / 64);
@@ -269,7 +284,7 @@ __global__ __launch_bounds__(kThreads) void cutoff_kernel(CutoffParams P0,
     const int32_t tx = tile % P.tiles[0];
     const int32_t ty = (tile / P.tiles[0]) % P.tiles[1];
     const int32_t tz = tile / (P.tiles[0] * P.tiles[1]);
-    const TileRows T = tile_rows(tx, ty, tz, P.n, P.h, P.o, P.b0, P.nb, P.bs, P.rc);
+    const TileRows T = tile_rows(tx, ty, tz, P.n, P.h, P.o, P.b0, P.nb, P.bs, P.list_rc);
 
     // This lane's nodes: an x-run of kNx nodes in one row of one plane; the
     // wave's 64 lanes cover 8 x 8 x (kTile / kWaves) nodes.
@@ -312,7 +327,7 @@ __global__ __launch_bounds__(kThreads) void cutoff_kernel(CutoffParams P0,
         int32_t local = 0;
         for (int32_t r = r_lo; r < r_hi; ++r) {
             int32_t cy, cz, cx0, cx1, cnt = 0, src = 0;
-            if (tile_row(T, row0 + r, P.b0, P.nb, P.bs, P.rc, &cy, &cz, &cx0, &cx1)) {
+            if (tile_row(T, row0 + r, P.b0, P.nb, P.bs, P.list_rc, &cy, &cz, &cx0, &cx1)) {
                 const int64_t base = ((int64_t)cz * P.nb[1] + cy) * P.nb[0];
                 int32_t s = bin_start[base + cx0];
                 int32_t e = bin_start[base + cx1 + 1];
@@ -385,10 +400,12 @@ __global__ __launch_bounds__(kThreads) void cutoff_kernel(CutoffParams P0,
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            if (use_clamp)
-                sweep<true>(stage, wave_list[wave], listed, x, y, z, P, acc);
+            if (mode == kSmoothClamp)
+                sweep<kSmoothClamp>(stage, wave_list[wave], listed, x, y, z, P, acc);
+            else if (mode == kSmoothSelect)
+                sweep<kSmoothSelect>(stage, wave_list[wave], listed, x, y, z, P, acc);
             else
-                sweep<false>(stage, wave_list[wave], listed, x, y, z, P, acc);
+                sweep<kTruncated>(stage, wave_list[wave], listed, x, y, z, P, acc);
             __syncthreads();
         }
     }
@@ -407,9 +424,11 @@ int32_t ceil_div32(int32_t a, int32_t b) { return (a + b - 1) / b; }
 }  // namespace
 
 hipError_t launch_cutoff(const void *workspace, const BinLayout &L, int64_t n_atoms,
-                         const Lattice &lat, const BinGeometry &g, float *V, hipStream_t stream)
+                         const Lattice &lat, const BinGeometry &g, int32_t term, float *V,
+                         hipStream_t stream)
 {
     CutoffParams P;
+    P.truncated = term == CPMAP_TERM_TRUNCATED;
     P.h = lat.h;
     for (int a = 0; a < 3; ++a) {
         P.o[a] = lat.o[a];
@@ -422,6 +441,11 @@ hipError_t launch_cutoff(const void *workspace, const BinLayout &L, int64_t n_at
     P.bs = g.bin_size;
     P.rc = g.cutoff;
     P.rc2 = g.cutoff * g.cutoff;
+    // The truncated term's fp32 inclusion test can keep an atom whose exact
+    // distance exceeds rc by an ulp, or whose bin rounding moved it across a
+    // face: widen its neighbourhood by a relative 2^-16 so that no kept atom
+    // is missed.  The smoothed term is ~1e-20 q there and needs no margin.
+    P.list_rc = P.truncated ? g.cutoff * (1.0f + 1.0f / 65536.0f) : g.cutoff;
     P.gc0 = (float)(15.0 / (8.0 * rc));
     P.gc1 = (float)(-5.0 / (4.0 * rc * rc * rc));
     P.gc2 = (float)(3.0 / (8.0 * rc * rc * rc * rc * rc));

@@ -225,6 +225,33 @@ cpmap_status cpmap_cutoff(const void *workspace, size_t workspace_bytes, int64_t
                           float bin_size, float cutoff,
                           float *V, void *stream);
 
+/* Terms of the cutoff sum. */
+enum {
+    CPMAP_TERM_SMOOTHED = 0,  /* q (1/r - gamma(r^2)), as cpmap_cutoff */
+    CPMAP_TERM_TRUNCATED = 1  /* q / r */
+};
+
+/*
+ * cpmap_cutoff_term -- cpmap_cutoff with a choice of term.
+ *
+ * CPMAP_TERM_SMOOTHED is cpmap_cutoff.  CPMAP_TERM_TRUNCATED sums q / r over
+ * the atoms with r^2 < rc^2 (the case-study notes' section 18.5 listing: the
+ * bin scan adds q * rsqrt(r2) only when r2 < rcut2).  The inclusion test is
+ * taken in fp32 exactly as r2 = fma(dx, dx, fma(dy, dy, dz*dz)) < fl(rc*rc),
+ * with dx, dy, dz the fp32 differences node - atom, so that an atom at the
+ * boundary is kept or dropped the same way on every call; the kept terms use
+ * the hardware reciprocal square root.  The neighbourhood of bins is widened
+ * by a relative 2^-16 for this term so that no kept atom is missed.
+ *
+ *   term   CPMAP_TERM_SMOOTHED or CPMAP_TERM_TRUNCATED (else CPMAP_EINVAL)
+ * Other arguments, ownership and errors as cpmap_cutoff.
+ */
+cpmap_status cpmap_cutoff_term(const void *workspace, size_t workspace_bytes, int64_t n_atoms,
+                               int32_t nx, int32_t ny, int32_t nz, float spacing,
+                               float ox, float oy, float oz,
+                               float bin_size, float cutoff, int32_t term,
+                               float *V, void *stream);
+
 /*
  * cpmap_neighbor_spans -- the neighbourhood the cutoff kernel walks for one
  * tile, for inspection and tests.  Host only, no HIP call.

@@ -36,6 +36,9 @@ def _load():
     lib.oracle_cutoff.restype = None
     lib.oracle_cutoff.argtypes = [_f32p, _i64, _i32, _i32, _i32, _f32, _f32, _f32, _f32, _f32,
                                   ctypes.c_void_p, _i64, _f64p, ctypes.c_void_p]
+    lib.oracle_cutoff_hard.restype = None
+    lib.oracle_cutoff_hard.argtypes = [_f32p, _i64, _i32, _i32, _i32, _f32, _f32, _f32, _f32,
+                                       _f32, ctypes.c_void_p, _i64, _f64p, ctypes.c_void_p]
     lib.oracle_smoothed_term.restype = ctypes.c_double
     lib.oracle_smoothed_term.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_double]
     lib.oracle_bin_grid.restype = _i32
@@ -102,6 +105,20 @@ def cutoff(atoms, dims, spacing, origin, rc, nodes=None, with_scale=False):
                       float(origin[0]), float(origin[1]), float(origin[2]), float(rc),
                       None if idx is None else idx.ctypes.data, m, V,
                       None if S is None else S.ctypes.data)
+    return (V, S) if with_scale else V
+
+
+def cutoff_hard(atoms, dims, spacing, origin, rc, nodes=None, with_scale=False):
+    """fp64 hard-truncated cutoff sum: q/r over the atoms whose fp32 r^2 < fp32 rc^2."""
+    lib = _load()
+    a = _atoms(atoms)
+    idx, m = _nodes(nodes, dims)
+    V = np.empty(m, dtype=np.float64)
+    S = np.empty(m, dtype=np.float64) if with_scale else None
+    lib.oracle_cutoff_hard(a, a.shape[0], int(dims[0]), int(dims[1]), int(dims[2]),
+                           float(spacing), float(origin[0]), float(origin[1]), float(origin[2]),
+                           float(rc), None if idx is None else idx.ctypes.data, m, V,
+                           None if S is None else S.ctypes.data)
     return (V, S) if with_scale else V
 
 

@@ -13,7 +13,8 @@
  *     every point g of a regular 3D lattice.
  *   - same page, section 18.2 (gather kernel listing): node (gx,gy,gz) sits at
  *     (gx,gy,gz)*h, lattice stored x-fastest, idx = (gz*Ny + gy)*Nx + gx.
- *   - same page, section 18.5: cutoff binning, "r2 < rcut2" is the test.
+ *   - same page, section 18.5: cutoff binning, "r2 < rcut2" is the test, and
+ *     the listing adds q/r for the kept atoms (the hard-truncated term).
  *   - "Input Binning Lecture Chapter 2", large-bin kernel slide (slide 24):
  *     the short-range term q*(1/r - g(r2)) with g(r2) = GC0 + r2*(GC1 +
  *     r2*GC2), used only when r2 < CUTOFF2.  The constants GC0..GC2 are not
@@ -34,6 +35,12 @@
  *       fp64 from the fp32 inputs.
  *   R4  the tolerance scale returned beside V is S = sum |q|/r over the atoms
  *       the sum keeps.
+ *   R6  the hard-truncated cutoff (the notes' section 18.5 listing: q/r added
+ *       only when r2 < rcut2) decides inclusion in fp32, exactly as the GPU
+ *       kernel forms r2: dx, dy, dz = fl32(node - atom), r2 = fma(dx, dx,
+ *       fma(dy, dy, fl32(dz*dz))), kept iff r2 < fl32(rc*rc).  The kept terms
+ *       are summed in fp64.  (An inclusion decision is integer work, so both
+ *       sides take it in the same precision.)
  *   R5  binning: halo H = ceil(rc/bs) bins on each side of the lattice; bin
  *       grid origin b0 = fl(o - H*bs) per axis; atom bin coordinate
  *       t = fl(fl(p - b0) / bs) in fp32; the atom is kept iff 0 <= t < nb on
@@ -184,6 +191,56 @@ void oracle_cutoff(const float *atoms, int64_t n_atoms,
                 v += smoothed_term(q, r2, rcd);
                 s += fabs(q) / sqrt(r2);
             }
+        }
+        V[t] = v;
+        if (S)
+            S[t] = s;
+    }
+}
+
+/* Inclusion test of the hard-truncated cutoff (reading R6), all fp32. */
+static int hard_keep(float x, float y, float z, const float *a, float rc2f)
+{
+    const float dx = x - a[0];
+    const float dy = y - a[1];
+    const float dz = z - a[2];
+    const float dz2 = dz * dz;
+    const float r2 = fmaf(dx, dx, fmaf(dy, dy, dz2));
+    return r2 < rc2f;
+}
+
+/*
+ * Hard-truncated cutoff sum (the notes' section 18.5 listing; reading R6):
+ * V = sum of q/r over the atoms the fp32 test keeps, r and the sum in fp64.
+ * S receives sum |q|/r over the same atoms.
+ */
+void oracle_cutoff_hard(const float *atoms, int64_t n_atoms,
+                        int32_t nx, int32_t ny, int32_t nz, float h,
+                        float ox, float oy, float oz, float rc,
+                        const int64_t *nodes, int64_t n_nodes,
+                        double *V, double *S)
+{
+    (void)nz;
+    const float rc2f = rc * rc;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t t = 0; t < n_nodes; ++t) {
+        int64_t g = nodes ? nodes[t] : t;
+        int64_t i, j, k;
+        split_index(g, nx, ny, &i, &j, &k);
+        const float xf = fmaf((float)i, h, ox);
+        const float yf = fmaf((float)j, h, oy);
+        const float zf = fmaf((float)k, h, oz);
+        double v = 0.0, s = 0.0;
+        for (int64_t a = 0; a < n_atoms; ++a) {
+            if (!hard_keep(xf, yf, zf, &atoms[4 * a], rc2f))
+                continue;
+            const double dx = (double)xf - (double)atoms[4 * a + 0];
+            const double dy = (double)yf - (double)atoms[4 * a + 1];
+            const double dz = (double)zf - (double)atoms[4 * a + 2];
+            const double q = (double)atoms[4 * a + 3];
+            const double r = sqrt(dx * dx + dy * dy + dz * dz);
+            v += q / r;
+            s += fabs(q) / r;
         }
         V[t] = v;
         if (S)

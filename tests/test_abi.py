@@ -101,6 +101,9 @@ def test_bin_and_cutoff_argument_checks():
     assert lib.cpmap_cutoff(ws, need - 1, 100, *LAT, 1.0, 2.0, FAKE, None) == ENOSPC
     assert lib.cpmap_cutoff(ws, need, 100, *LAT, 1.0, 2.0, None, None) == EINVAL
     assert lib.cpmap_cutoff(None, need, 100, *LAT, 1.0, 2.0, FAKE, None) == EINVAL
+    assert lib.cpmap_cutoff_term(ws, need, 100, *LAT, 1.0, 2.0, 2, FAKE, None) == EINVAL
+    assert lib.cpmap_cutoff_term(ws, need, 100, *LAT, 1.0, 2.0, -1, FAKE, None) == EINVAL
+    assert lib.cpmap_cutoff_term(ws, need, 100, *LAT, 1.0, 2.0, 1, FAKE, None) == EGEOM
 
 
 def test_layout_query_errors():

@@ -184,3 +184,63 @@ def test_cutoff_matches_direct_minus_gamma_for_huge_cutoff(torch):
     V = cpmap.cutoff(ws, 3000, lat, 8.0, rc).cpu().numpy().reshape(-1)
     Vo, S = oracle.cutoff(atoms_np, lat.dims, lat.spacing, lat.origin, rc, with_scale=True)
     _parity(V, Vo, S, "huge rc")
+
+
+# ---------------------------------------------------------------- truncated term
+
+@pytest.mark.parametrize("case", CUT_CASES, ids=[f"n{c[0]}_{c[1].nx}x{c[1].ny}x{c[1].nz}_bs{c[2]}" for c in CUT_CASES])
+def test_truncated_small_all_nodes(torch, case):
+    n, lat, bs, rc, lo, hi, seed = case
+    print(f"[truncated] n={n} dims={lat.dims} bs={bs} rc={rc}", flush=True)
+    atoms_np = wl.random_atoms(n, lo, hi, seed=seed)
+    atoms = torch.from_numpy(atoms_np).cuda()
+    ws = cpmap.bin_atoms(atoms, lat, bs, rc)
+    V = cpmap.cutoff(ws, n, lat, bs, rc, term="truncated").cpu().numpy().reshape(-1)
+    Vo, S = oracle.cutoff_hard(atoms_np, lat.dims, lat.spacing, lat.origin, rc, with_scale=True)
+    _parity(V, Vo, S, f"truncated n={n} dims={lat.dims}")
+
+
+def test_truncated_boundary_decisions(torch):
+    """Atoms one fp32 ulp inside, exactly at and one ulp outside rc of lattice
+    nodes (along each axis), plus bin faces: the kernel keeps and drops
+    exactly the atoms the oracle's fp32 test does."""
+    h = np.float32(0.7)  # rc / h is not an integer: no atom lands on a node
+    lat = Lattice(16, 16, 16, float(h))
+    rc = 3.0
+    pts = []
+    rng = np.random.default_rng(21)
+    for _ in range(300):
+        node = rng.integers(0, 16, size=3).astype(np.float32) * h  # one fp32 rounding
+        ax = int(rng.integers(0, 3))
+        sgn = 1.0 if rng.random() < 0.5 else -1.0
+        for r in (np.nextafter(np.float32(rc), np.float32(0)), np.float32(rc),
+                  np.nextafter(np.float32(rc), np.float32(10))):
+            p = node.astype(np.float32).copy()
+            p[ax] = np.float32(p[ax] + sgn * r)
+            pts.append([*p, rng.uniform(-1, 1)])
+    atoms_np = np.array(pts, dtype=np.float32)
+    atoms = torch.from_numpy(atoms_np).cuda()
+    ws = cpmap.bin_atoms(atoms, lat, 1.0, rc)
+    V = cpmap.cutoff(ws, atoms_np.shape[0], lat, 1.0, rc, term="truncated").cpu().numpy().reshape(-1)
+    Vo, S = oracle.cutoff_hard(atoms_np, lat.dims, lat.spacing, lat.origin, rc, with_scale=True)
+    _parity(V, Vo, S, "truncated boundary")
+
+
+def test_truncated_config5_checked_nodes(torch):
+    w = wl.cutoff_binned()
+    lat = w.lattice
+    atoms = torch.from_numpy(w.atoms).cuda()
+    ws = cpmap.bin_atoms(atoms, lat, w.bin_size, w.cutoff)
+    V = cpmap.cutoff(ws, w.n_atoms, lat, w.bin_size, w.cutoff, term="truncated").cpu().numpy().reshape(-1)
+    nodes = wl.checked_nodes(lat)
+    Vo, S = oracle.cutoff_hard(w.atoms, lat.dims, lat.spacing, lat.origin, w.cutoff, nodes=nodes,
+                               with_scale=True)
+    worst = _parity(V[nodes], Vo, S, w.name + " truncated")
+    print(f"{w.name} truncated: {nodes.size} nodes, worst |err|/S = {worst:.3e}")
+
+
+def test_cutoff_rejects_unknown_term(torch):
+    lat = Lattice(8, 8, 8, 0.5)
+    ws = cpmap.bin_atoms(torch.zeros((4, 4), device="cuda"), lat, 1.0, 2.0)
+    with pytest.raises(ValueError):
+        cpmap.cutoff(ws, 4, lat, 1.0, 2.0, term="hard")

@@ -319,3 +319,53 @@ def test_bin_atoms_is_a_stable_sort_with_correct_boxes():
     gap = np.maximum(0, np.maximum(lat_lo - D, D - lat_hi))
     assert np.all(np.sqrt((gap**2).sum(1)) >= rc - 1e-4)
     assert (~kept).sum() > 0 and kept.sum() > 0
+
+
+# ---------------------------------------------------------------- hard-truncated cutoff
+
+def test_cutoff_hard_single_atom_values_and_tie():
+    """q/r inside (r = 6 -> exactly 1/6), nothing at the tie r = rc (strict
+    test) or beyond (the notes' section 18.5 listing)."""
+    atoms = np.array([[0.0, 0.0, 0.0, 1.0]], dtype=np.float32)
+    V, S = oracle.cutoff_hard(atoms, (1, 1, 3), 6.0, (0.0, 0.0, 6.0), 12.0, with_scale=True)
+    assert V[0] == 1.0 / 6.0 and S[0] == 1.0 / 6.0
+    assert V[1] == 0.0 and V[2] == 0.0 and S[1] == 0.0
+
+
+def test_cutoff_hard_decision_is_taken_in_fp32():
+    """Reading R6: an atom one fp32 ulp inside rc along x is kept (its fp32
+    r^2 rounds below 144), one ulp outside is not; the kept value is q/r with
+    r the exact fp64 distance."""
+    inside = np.nextafter(np.float32(12.0), np.float32(0.0))
+    outside = np.nextafter(np.float32(12.0), np.float32(100.0))
+    assert np.float32(inside) * np.float32(inside) < np.float32(144.0)
+    atoms_in = np.array([[inside, 0.0, 0.0, 0.5]], dtype=np.float32)
+    atoms_out = np.array([[outside, 0.0, 0.0, 0.5]], dtype=np.float32)
+    Vi = oracle.cutoff_hard(atoms_in, (1, 1, 1), 1.0, (0.0, 0.0, 0.0), 12.0)
+    Vo = oracle.cutoff_hard(atoms_out, (1, 1, 1), 1.0, (0.0, 0.0, 0.0), 12.0)
+    assert Vi[0] == 0.5 / float(inside)
+    assert Vo[0] == 0.0
+
+
+def test_cutoff_hard_with_huge_cutoff_is_the_direct_sum():
+    """With rc beyond every distance every atom is kept, and the kept terms
+    are summed exactly as the direct sum sums them: bit-identical results."""
+    A = random_atoms(500, (-3, -3, -3), (9, 9, 9), seed=91)
+    dims, h, o = (7, 6, 5), 0.75, (0.25, -0.5, 0.0)
+    np.testing.assert_array_equal(oracle.cutoff_hard(A, dims, h, o, 1.0e4),
+                                  oracle.direct(A, dims, h, o))
+
+
+def test_cutoff_hard_shells():
+    """Shells at r = 3 and 6 inside rc = 12, 13 and 20 outside: V = 6 (q1/3 + q2/6)."""
+    c = np.array([10.0, 10.0, 10.0])
+    pts = []
+    for r, q in [(3.0, 0.5), (6.0, -0.25), (13.0, 1.0), (20.0, -1.0)]:
+        for ax in range(3):
+            for sg in (-1, 1):
+                p = c.copy()
+                p[ax] += sg * r
+                pts.append([*p, q])
+    atoms = np.array(pts, dtype=np.float32)
+    V = oracle.cutoff_hard(atoms, (1, 1, 1), 1.0, tuple(c), 12.0)
+    assert V[0] == pytest.approx(6 * (0.5 / 3 - 0.25 / 6), rel=1e-14)
