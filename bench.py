@@ -188,7 +188,21 @@ def main():
             "kernel_ms_min": min(per),
             "flop_per_eval": FLOP_PER_EVAL,
         }
-        del atoms, V, ws
+        # ion placement on the map just computed: argmin / argmax over 8M nodes
+        ext_ws = torch.empty(cpmap.library().cpmap_extrema_workspace_bytes(lat.n_points),
+                             dtype=torch.uint8, device=dev)
+        ext_out = (torch.empty(2, dtype=torch.int64, device=dev),
+                   torch.empty(2, dtype=torch.float32, device=dev))
+        _, per_ext = time_launches(torch, lambda: cpmap.extrema(V, workspace=ext_ws, out=ext_out),
+                                   max(args.steps, 10), args.warmup)
+        ext_ms = statistics.median(per_ext)
+        result["ion_placement"] = {
+            "op": "argmin/argmax of V (cpmap_extrema)",
+            "ms_median": ext_ms,
+            "hbm_gbs_algorithmic": 4 * lat.n_points / (ext_ms * 1e-3) / 1e9,
+            "peak_gbs": PEAK_HBM_GBS,
+        }
+        del atoms, V, ws, ext_ws
 
     if not args.no_cutoff and args.only in (None, "cutoff"):
         result["cutoff"] = bench_cutoff(torch, cpmap, wl, dev, args)

@@ -24,7 +24,7 @@ from .workloads import Lattice
 __all__ = [
     "Lattice", "CpmapError", "direct", "direct_workspace_bytes", "direct_plan", "bin_atoms", "cutoff", "bin_workspace_bytes",
     "bin_grid", "workspace_layout", "workspace_views", "neighbor_spans", "library",
-    "library_path", "header_functions", "STATUS",
+    "library_path", "header_functions", "STATUS", "extrema", "place_ions", "TERMS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -62,6 +62,8 @@ _SIGNATURES = {
                                       ctypes.POINTER(_i64)]),
     "cpmap_cutoff": (_i32, [_vp, _sz, _i64, *_LAT, _f32, _f32, _vp, _vp]),
     "cpmap_cutoff_term": (_i32, [_vp, _sz, _i64, *_LAT, _f32, _f32, _i32, _vp, _vp]),
+    "cpmap_extrema_workspace_bytes": (_sz, [_i64]),
+    "cpmap_extrema": (_i32, [_vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "cpmap_neighbor_spans": (_i64, [*_LAT, _f32, _f32, _i32, _i32, _i32, ctypes.POINTER(_i32),
                                     _i64]),
 }
@@ -270,3 +272,44 @@ def neighbor_spans(lat: Lattice, bin_size: float, cutoff: float, tile: Tuple[int
     if n > max_spans:
         return neighbor_spans(lat, bin_size, cutoff, tile, int(n))
     return [tuple(buf[4 * i:4 * i + 4]) for i in range(n)]
+
+
+def extrema(V, workspace=None, out=None):
+    """Argmin / argmax of a GPU float32 map (cpmap_extrema).
+
+    Returns an int64 tensor [argmin, argmax] and a float32 tensor [vmin, vmax],
+    both on V's device (no synchronisation).
+    """
+    torch = _torch()
+    if V.dtype != torch.float32 or not V.is_cuda or not V.is_contiguous():
+        raise ValueError("V must be a contiguous float32 GPU tensor")
+    n = V.numel()
+    need = int(library().cpmap_extrema_workspace_bytes(n))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=V.device)
+    idx = torch.empty(2, dtype=torch.int64, device=V.device) if out is None else out[0]
+    val = torch.empty(2, dtype=torch.float32, device=V.device) if out is None else out[1]
+    st = library().cpmap_extrema(V.data_ptr() if n else None, n, idx.data_ptr(), val.data_ptr(),
+                                 workspace.data_ptr(), workspace.numel(), _stream_ptr(V.device))
+    _check("cpmap_extrema", st)
+    return idx, val
+
+
+def place_ions(V, lat: Lattice):
+    """Nodes for a positive ion (lowest potential) and a negative ion (highest),
+    as ((i, j, k), (x, y, z), value) pairs; synchronises to read them back."""
+    idx, val = extrema(V)
+    idx = idx.cpu().tolist()
+    val = val.cpu().tolist()
+    out = []
+    for g, v in zip(idx, val):
+        if g < 0:
+            out.append(None)
+            continue
+        i, j, k = g % lat.nx, (g // lat.nx) % lat.ny, g // (lat.nx * lat.ny)
+        import numpy as np
+        h = float(np.float32(lat.spacing))
+        pos = tuple(float(np.float32(float(np.float32(o)) + c * h))  # one rounding, as the kernels
+                    for o, c in zip(lat.origin, (i, j, k)))
+        out.append(((i, j, k), pos, v))
+    return {"positive_ion": out[0], "negative_ion": out[1]}

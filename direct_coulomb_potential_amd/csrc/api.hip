@@ -355,4 +355,31 @@ cpmap_status cpmap_cutoff(const void *workspace, size_t workspace_bytes, int64_t
                              bin_size, cutoff, CPMAP_TERM_SMOOTHED, V, stream);
 }
 
+size_t cpmap_extrema_workspace_bytes(int64_t n)
+{
+    if (n < 0 || n > CPMAP_MAX_POINTS)
+        return 0;
+    return extrema_workspace_bytes(n);
+}
+
+cpmap_status cpmap_extrema(const float *V, int64_t n, int64_t *out_index, float *out_value,
+                           void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (n < 0)
+        return CPMAP_EINVAL;
+    if (n > CPMAP_MAX_POINTS)
+        return CPMAP_ERANGE;
+    if ((n > 0 && V == nullptr) || out_index == nullptr || out_value == nullptr ||
+        workspace == nullptr)
+        return CPMAP_EINVAL;
+    if (!aligned(V, 4) || !aligned(out_index, 8) || !aligned(out_value, 4) ||
+        !aligned(workspace, 256))
+        return CPMAP_EINVAL;
+    if (workspace_bytes < extrema_workspace_bytes(n))
+        return CPMAP_ENOSPC;
+    hipError_t e = launch_extrema(V, n, out_index, out_value, workspace,
+                                  static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? CPMAP_OK : CPMAP_EHIP;
+}
+
 }  // extern "C"

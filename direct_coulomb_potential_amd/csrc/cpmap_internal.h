@@ -86,7 +86,12 @@ hipError_t launch_cutoff(const void *workspace, const BinLayout &L, int64_t n_at
                          const Lattice &lat, const BinGeometry &g, int32_t term, float *V,
                          hipStream_t stream);
 
-// Neighbourhood of one 8x8x8 tile as x-runs of bins; host and device.
+// Argmin / argmax of a map (ion placement).
+size_t extrema_workspace_bytes(int64_t n);
+hipError_t launch_extrema(const float *V, int64_t n, int64_t *out_index, float *out_value,
+                          void *workspace, hipStream_t stream);
+
+// Nodes per tile edge of the cutoff kernel.
 constexpr int kTile = 8;
 
 }  // namespace cpmap

@@ -271,6 +271,34 @@ int64_t cpmap_neighbor_spans(int32_t nx, int32_t ny, int32_t nz, float spacing,
                              int32_t tx, int32_t ty, int32_t tz,
                              int32_t *spans_out, int64_t max_spans);
 
+/*
+ * cpmap_extrema_workspace_bytes -- workspace of cpmap_extrema for n values
+ * (at most 64 KB).  Host only, no HIP call; 0 on invalid n.
+ */
+size_t cpmap_extrema_workspace_bytes(int64_t n);
+
+/*
+ * cpmap_extrema -- ion placement on a potential map (the case-study notes'
+ * section 18.1: positive ions are placed where the potential is lowest,
+ * negative ions where it is highest).
+ *
+ * Writes, on the device, out_index[0] = argmin and out_index[1] = argmax of
+ * V[0..n) and out_value[0..1] = the values there.  NaN values are skipped;
+ * among equal values the smallest index wins (+0 and -0 are equal); with no
+ * non-NaN value both indices are -1 and both values NaN.  A linear index of
+ * a lattice map gives the node as i = idx % nx, j = (idx / nx) % ny,
+ * k = idx / (nx * ny).
+ *
+ *   V          device, n floats (any layout; read only)
+ *   out_index  device, 2 int64 (8-byte aligned), written
+ *   out_value  device, 2 floats, written
+ *   workspace  device, >= cpmap_extrema_workspace_bytes(n), 256-byte aligned
+ * Deterministic: the result does not depend on the order in which partial
+ * results are combined.
+ */
+cpmap_status cpmap_extrema(const float *V, int64_t n, int64_t *out_index, float *out_value,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

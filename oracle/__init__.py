@@ -47,6 +47,9 @@ def _load():
     lib.oracle_bin_atoms.restype = _i64
     lib.oracle_bin_atoms.argtypes = [_f32p, _i64, _i32, _i32, _i32, _f32, _f32, _f32, _f32,
                                      _f32, _f32, _i32p, _f32p, ctypes.c_void_p]
+    lib.oracle_extrema.restype = None
+    lib.oracle_extrema.argtypes = [_f32p, _i64, np.ctypeslib.ndpointer(dtype=np.int64),
+                                   _f32p]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
     _lib = lib
@@ -160,3 +163,14 @@ def bin_atoms(atoms, dims, spacing, origin, bin_size, cutoff_radius):
     if kept < 0:
         raise ValueError("invalid bin geometry")
     return starts, out[:kept].copy(), bin_of[:a.shape[0]].copy()
+
+
+def extrema(V):
+    """Ion-placement extrema of a potential map: ((argmin, argmax), (vmin, vmax)),
+    smallest index among ties, NaN nodes skipped, -1 when all are NaN."""
+    lib = _load()
+    v = np.ascontiguousarray(V, dtype=np.float32).reshape(-1)
+    idx = np.zeros(2, dtype=np.int64)
+    val = np.zeros(2, dtype=np.float32)
+    lib.oracle_extrema(v, v.size, idx, val)
+    return (int(idx[0]), int(idx[1])), (float(val[0]), float(val[1]))

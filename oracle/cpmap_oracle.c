@@ -41,6 +41,10 @@
  *       fma(dy, dy, fl32(dz*dz))), kept iff r2 < fl32(rc*rc).  The kept terms
  *       are summed in fp64.  (An inclusion decision is integer work, so both
  *       sides take it in the same precision.)
+ *   R7  ion placement (the notes' section 18.1: positive ions go where the
+ *       potential is lowest, negative ions where it is highest): the extrema
+ *       of V over its non-NaN nodes; among equal values the smallest node
+ *       index; -1 when every node is NaN.
  *   R5  binning: halo H = ceil(rc/bs) bins on each side of the lattice; bin
  *       grid origin b0 = fl(o - H*bs) per axis; atom bin coordinate
  *       t = fl(fl(p - b0) / bs) in fp32; the atom is kept iff 0 <= t < nb on
@@ -352,4 +356,28 @@ int64_t oracle_bin_atoms(const float *atoms, int64_t n_atoms,
     free(fill);
     free(ids);
     return bin_start[nbins];
+}
+
+/*
+ * Extrema of a potential map for ion placement (reading R7).  out_index[0] =
+ * argmin, out_index[1] = argmax (smallest index among equal values, NaN
+ * nodes skipped, -1 when there is no non-NaN node); out_value[0..1] = the
+ * values at those nodes (NaN when the index is -1).
+ */
+void oracle_extrema(const float *V, int64_t n, int64_t *out_index, float *out_value)
+{
+    int64_t imin = -1, imax = -1;
+    for (int64_t i = 0; i < n; ++i) {
+        const float v = V[i];
+        if (isnan(v))
+            continue;
+        if (imin < 0 || v < V[imin])
+            imin = i;
+        if (imax < 0 || v > V[imax])
+            imax = i;
+    }
+    out_index[0] = imin;
+    out_index[1] = imax;
+    out_value[0] = imin >= 0 ? V[imin] : NAN;
+    out_value[1] = imax >= 0 ? V[imax] : NAN;
 }

@@ -144,3 +144,18 @@ def test_direct_workspace_queries_and_checks():
     out = (ctypes.c_int32 * 5)()
     assert lib.cpmap_direct_plan(10, 2, 2, 2, 1, None) == EINVAL
     assert lib.cpmap_direct_plan(-1, 2, 2, 2, 1, out) == EINVAL
+
+
+def test_extrema_argument_checks():
+    lib = cpmap.library()
+    need = lib.cpmap_extrema_workspace_bytes(8_000_000)
+    assert 0 < need <= 64 * 1024
+    assert lib.cpmap_extrema_workspace_bytes(-1) == 0
+    ws = ctypes.c_void_p(0x100000)
+    out_i, out_v = ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000)
+    assert lib.cpmap_extrema(FAKE, 8_000_000, out_i, out_v, ws, need - 1, None) == ENOSPC
+    assert lib.cpmap_extrema(FAKE, -1, out_i, out_v, ws, need, None) == EINVAL
+    assert lib.cpmap_extrema(None, 10, out_i, out_v, ws, need, None) == EINVAL
+    assert lib.cpmap_extrema(FAKE, 10, None, out_v, ws, need, None) == EINVAL
+    assert lib.cpmap_extrema(FAKE, 10, ctypes.c_void_p(0x2004), out_v, ws, need, None) == EINVAL
+    assert lib.cpmap_extrema(FAKE, 10, out_i, out_v, None, need, None) == EINVAL

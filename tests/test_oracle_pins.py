@@ -369,3 +369,31 @@ def test_cutoff_hard_shells():
     atoms = np.array(pts, dtype=np.float32)
     V = oracle.cutoff_hard(atoms, (1, 1, 1), 1.0, tuple(c), 12.0)
     assert V[0] == pytest.approx(6 * (0.5 / 3 - 0.25 / 6), rel=1e-14)
+
+
+# ---------------------------------------------------------------- ion placement extrema
+
+def _golden_values(vals):
+    return np.array([float(v) for v in vals], dtype=np.float32)
+
+
+def test_extrema_golden(golden_dir):
+    """Hand-worked argmin/argmax with ties, NaN, +-inf and +-0 (reading R7)."""
+    with open(os.path.join(golden_dir, "extrema.json")) as f:
+        fx = json.load(f)
+    for case in fx["cases"]:
+        V = _golden_values(case["V"])
+        (imin, imax), (vmin, vmax) = oracle.extrema(V)
+        assert (imin, imax) == (case["argmin"], case["argmax"]), case
+        if imin >= 0:
+            assert vmin == V[imin] and vmax == V[imax]
+
+
+def test_extrema_matches_numpy_nan_reductions():
+    """Against numpy's nanargmin / nanargmax (first occurrence, NaN skipped)."""
+    rng = np.random.default_rng(5)
+    for trial in range(20):
+        V = np.round(rng.normal(size=1000) * 4).astype(np.float32)  # many ties
+        V[rng.random(1000) < 0.05] = np.nan
+        (imin, imax), _ = oracle.extrema(V)
+        assert imin == int(np.nanargmin(V)) and imax == int(np.nanargmax(V))
