@@ -204,6 +204,9 @@ def main():
         }
         del atoms, V, ws, ext_ws
 
+    if args.only is None:
+        result["gather_vs_scatter"] = bench_scatter(torch, cpmap, wl, dev, args)
+
     if not args.no_cutoff and args.only in (None, "cutoff"):
         result["cutoff"] = bench_cutoff(torch, cpmap, wl, dev, args)
 
@@ -212,6 +215,28 @@ def main():
         result["cpu_baseline"] = cpu_baseline(oracle, w, args.cpu_seconds)
 
     print(json.dumps(result), flush=True)
+
+
+def bench_scatter(torch, cpmap, wl, dev, args):
+    """The gather (production) against the atomics-based scatter contrast on
+    the two 100x100x50-lattice workloads."""
+    out = {}
+    for w in (wl.plane_direct(), wl.full_direct()):
+        lat = w.lattice
+        atoms = torch.from_numpy(w.atoms).to(dev)
+        V = torch.empty((lat.nz, lat.ny, lat.nx), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(cpmap.direct_workspace_bytes(w.n_atoms, lat), 1), dtype=torch.uint8,
+                         device=dev)
+        _, per_g = time_launches(torch, lambda: cpmap.direct(atoms, lat, out=V, workspace=ws),
+                                 max(args.steps, 5), args.warmup)
+        _, per_s = time_launches(torch, lambda: cpmap.direct_scatter(atoms, lat, out=V),
+                                 max(args.steps, 5), args.warmup)
+        g_ms, s_ms = statistics.median(per_g), statistics.median(per_s)
+        out[w.name] = {"pairs": w.pairs, "gather_ms": g_ms, "scatter_ms": s_ms,
+                       "gather_G_evals_per_s": w.pairs / (g_ms * 1e-3) / 1e9,
+                       "scatter_G_evals_per_s": w.pairs / (s_ms * 1e-3) / 1e9,
+                       "scatter_over_gather": s_ms / g_ms}
+    return out
 
 
 def bench_cutoff(torch, cpmap, wl, dev, args):

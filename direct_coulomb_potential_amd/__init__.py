@@ -22,7 +22,7 @@ from typing import Optional, Tuple
 from .workloads import Lattice
 
 __all__ = [
-    "Lattice", "CpmapError", "direct", "direct_workspace_bytes", "direct_plan", "bin_atoms", "cutoff", "bin_workspace_bytes",
+    "Lattice", "CpmapError", "direct", "direct_scatter", "direct_workspace_bytes", "direct_plan", "bin_atoms", "cutoff", "bin_workspace_bytes",
     "bin_grid", "workspace_layout", "workspace_views", "neighbor_spans", "library",
     "library_path", "header_functions", "STATUS", "extrema", "place_ions", "TERMS",
 ]
@@ -55,6 +55,7 @@ _SIGNATURES = {
     "cpmap_direct_with_workspace": (_i32, [_vp, _i64, *_LAT, _vp, _vp, _sz, _vp]),
     "cpmap_direct_plan": (_i32, [_i64, _i32, _i32, _i32, _i32, ctypes.POINTER(_i32)]),
     "cpmap_direct_occupancy_check": (_i32, []),
+    "cpmap_direct_scatter": (_i32, [_vp, _i64, *_LAT, _vp, _vp]),
     "cpmap_bin_workspace_bytes": (_sz, [_i64, *_LAT, _f32, _f32]),
     "cpmap_bin_grid": (_i32, [*_LAT, _f32, _f32, ctypes.POINTER(_i32)]),
     "cpmap_bin_atoms": (_i32, [_vp, _i64, *_LAT, _f32, _f32, _vp, _sz, _vp]),
@@ -187,6 +188,18 @@ def direct(atoms, lat: Lattice, out=None, split: bool = True, workspace=None):
     st = library().cpmap_direct_with_workspace(a_ptr, atoms.shape[0], *_lat_args(lat), v_ptr,
                                                ws_ptr, ws_bytes, stream)
     _check("cpmap_direct_with_workspace", st)
+    return V
+
+
+def direct_scatter(atoms, lat: Lattice, out=None):
+    """The scatter form of the direct sum (atomics; a contrast, not bit-reproducible)."""
+    _check_atoms(atoms)
+    V = _out(lat, atoms.device, out)
+    st = library().cpmap_direct_scatter(atoms.data_ptr() if atoms.numel() else None,
+                                        atoms.shape[0], *_lat_args(lat),
+                                        V.data_ptr() if V.numel() else None,
+                                        _stream_ptr(atoms.device))
+    _check("cpmap_direct_scatter", st)
     return V
 
 

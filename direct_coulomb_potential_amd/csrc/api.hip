@@ -355,6 +355,29 @@ cpmap_status cpmap_cutoff(const void *workspace, size_t workspace_bytes, int64_t
                              bin_size, cutoff, CPMAP_TERM_SMOOTHED, V, stream);
 }
 
+cpmap_status cpmap_direct_scatter(const float *atoms, int64_t n_atoms, int32_t nx, int32_t ny,
+                                  int32_t nz, float spacing, float ox, float oy, float oz,
+                                  float *V, void *stream)
+{
+    if (n_atoms < 0)
+        return CPMAP_EINVAL;
+    if (n_atoms > CPMAP_MAX_ATOMS)
+        return CPMAP_ERANGE;
+    cpmap_status st = check_lattice(nx, ny, nz, spacing, ox, oy, oz);
+    if (st != CPMAP_OK)
+        return st;
+    const Lattice lat = make_lattice(nx, ny, nz, spacing, ox, oy, oz);
+    if (lat.points() == 0)
+        return CPMAP_OK;
+    if (V == nullptr || (n_atoms > 0 && atoms == nullptr))
+        return CPMAP_EINVAL;
+    if (!aligned(V, 4) || (atoms && !aligned(atoms, 16)))
+        return CPMAP_EINVAL;
+    hipError_t e = launch_scatter(reinterpret_cast<const float4 *>(atoms), n_atoms, lat, V,
+                                  static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? CPMAP_OK : CPMAP_EHIP;
+}
+
 size_t cpmap_extrema_workspace_bytes(int64_t n)
 {
     if (n < 0 || n > CPMAP_MAX_POINTS)

@@ -86,6 +86,10 @@ hipError_t launch_cutoff(const void *workspace, const BinLayout &L, int64_t n_at
                          const Lattice &lat, const BinGeometry &g, int32_t term, float *V,
                          hipStream_t stream);
 
+// Scatter form of the direct sum (atomics; a measured contrast).
+hipError_t launch_scatter(const float4 *atoms, int64_t n_atoms, const Lattice &lat, float *V,
+                          hipStream_t stream);
+
 // Argmin / argmax of a map (ion placement).
 size_t extrema_workspace_bytes(int64_t n);
 hipError_t launch_extrema(const float *V, int64_t n, int64_t *out_index, float *out_value,

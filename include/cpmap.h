@@ -85,6 +85,22 @@ cpmap_status cpmap_direct(const float *atoms, int64_t n_atoms,
                           float *V, void *stream);
 
 /*
+ * cpmap_direct_scatter -- the same sum in the scatter mapping, kept only as a
+ * measured contrast to the gather (the case-study notes' section 18.2: a
+ * thread per atom adds its q/r into every node with an atomic add).  One
+ * wave per atom; its lanes add into 64 adjacent nodes at a time with
+ * hardware fp32 atomics in L2.  V is zeroed, then accumulated.  The order in
+ * which atoms reach a node varies, so V meets the accuracy bound of
+ * cpmap_direct but is NOT bit-reproducible.  V must be ordinary device memory
+ * (hipMalloc / torch), where the hardware fp32 atomics are valid.  Arguments
+ * and errors as cpmap_direct.
+ */
+cpmap_status cpmap_direct_scatter(const float *atoms, int64_t n_atoms,
+                                  int32_t nx, int32_t ny, int32_t nz, float spacing,
+                                  float ox, float oy, float oz,
+                                  float *V, void *stream);
+
+/*
  * cpmap_direct_workspace_bytes -- size of the optional workspace that lets
  * cpmap_direct_with_workspace split the atom list across workgroups (0 when
  * the lattice and atom count gain nothing from it).  Host only, no HIP call;

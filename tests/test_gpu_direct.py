@@ -169,3 +169,30 @@ def test_direct_workload_checked_nodes(torch, index, split):
     Vo, S = oracle.direct(w.atoms, lat.dims, lat.spacing, lat.origin, nodes=nodes, with_scale=True)
     worst = _assert_parity(Vg[nodes], Vo, S, w.name)
     print(f"{w.name}: {nodes.size} nodes, worst |err|/S = {worst:.3e}")
+
+
+# ---------------------------------------------------------------- scatter contrast
+
+@pytest.mark.parametrize("case", CASES[:6], ids=[f"n{c[0]}_{c[1][0]}x{c[1][1]}x{c[1][2]}" for c in CASES[:6]])
+def test_scatter_small_all_nodes(torch, case):
+    """The atomics-based scatter meets the same bound (its summation order
+    varies from run to run)."""
+    n, dims, h, origin, lo, hi, seed = case
+    atoms_np = wl.random_atoms(n, lo, hi, seed=seed)
+    lat = Lattice(*dims, h, origin)
+    atoms = torch.from_numpy(atoms_np).cuda()
+    V = cpmap.direct_scatter(atoms, lat).cpu().numpy().reshape(-1)
+    Vo, S = oracle.direct(atoms_np, dims, h, origin, with_scale=True)
+    _assert_parity(V, Vo, S, f"scatter n={n} dims={dims}")
+
+
+@pytest.mark.parametrize("index", [1, 2])
+def test_scatter_workloads(torch, index):
+    w = wl.workload(index)
+    lat = w.lattice
+    atoms = torch.from_numpy(w.atoms).cuda()
+    out = torch.full((lat.nz, lat.ny, lat.nx), 5.0, device="cuda")  # must be overwritten
+    V = cpmap.direct_scatter(atoms, lat, out=out).cpu().numpy().reshape(-1)
+    Vo, S = oracle.direct(w.atoms, lat.dims, lat.spacing, lat.origin, with_scale=True)
+    worst = _assert_parity(V, Vo, S, "scatter " + w.name)
+    print(f"scatter {w.name}: worst |err|/S = {worst:.3e}")
