@@ -159,3 +159,17 @@ def test_extrema_argument_checks():
     assert lib.cpmap_extrema(FAKE, 10, None, out_v, ws, need, None) == EINVAL
     assert lib.cpmap_extrema(FAKE, 10, ctypes.c_void_p(0x2004), out_v, ws, need, None) == EINVAL
     assert lib.cpmap_extrema(FAKE, 10, out_i, out_v, None, need, None) == EINVAL
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch):
+    """No CPU fallback: with libcpmap.so missing every call raises."""
+    import numpy as np
+    torch = pytest.importorskip("torch")
+    monkeypatch.setattr(cpmap, "_lib", None)
+    monkeypatch.setattr(cpmap, "_LIB_PATH", "/nonexistent/libcpmap.so")
+    with pytest.raises(ImportError):
+        cpmap.library()
+    with pytest.raises(ImportError):
+        cpmap.direct_workspace_bytes(10, Lattice(2, 2, 2, 0.5))
+    with pytest.raises((ImportError, ValueError)):
+        cpmap.direct(torch.from_numpy(np.zeros((1, 4), np.float32)), Lattice(2, 2, 2, 0.5))
