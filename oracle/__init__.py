@@ -47,6 +47,9 @@ def _load():
     lib.oracle_bin_atoms.restype = _i64
     lib.oracle_bin_atoms.argtypes = [_f32p, _i64, _i32, _i32, _i32, _f32, _f32, _f32, _f32,
                                      _f32, _f32, _i32p, _f32p, ctypes.c_void_p]
+    lib.oracle_bin_slots.restype = _i64
+    lib.oracle_bin_slots.argtypes = [_f32p, _i64, _i32, _i32, _i32, _f32, _f32, _f32, _f32,
+                                     _f32, _f32, _i32, _f32p, _i32p, _f32p]
     lib.oracle_extrema.restype = None
     lib.oracle_extrema.argtypes = [_f32p, _i64, np.ctypeslib.ndpointer(dtype=np.int64),
                                    _f32p]
@@ -163,6 +166,29 @@ def bin_atoms(atoms, dims, spacing, origin, bin_size, cutoff_radius):
     if kept < 0:
         raise ValueError("invalid bin geometry")
     return starts, out[:kept].copy(), bin_of[:a.shape[0]].copy()
+
+
+def bin_slots(atoms, dims, spacing, origin, bin_size, cutoff_radius, capacity):
+    """Fixed-capacity bins with an overflow list (reading R16).
+
+    Returns (slots (nbins, capacity, 4) float32 with empty slots (inf, inf,
+    inf, 0), over_start[nbins+1] int32, overflow atoms (n_over, 4) float32
+    grouped by bin).
+    """
+    lib = _load()
+    a = _atoms(atoms)
+    bd, _, _ = bin_grid(dims, spacing, origin, bin_size, cutoff_radius)
+    nbins = bd[0] * bd[1] * bd[2]
+    slots = np.zeros((nbins, int(capacity), 4), dtype=np.float32)
+    starts = np.zeros(nbins + 1, dtype=np.int32)
+    over = np.zeros((max(a.shape[0], 1), 4), dtype=np.float32)
+    n_over = lib.oracle_bin_slots(a, a.shape[0], int(dims[0]), int(dims[1]), int(dims[2]),
+                                  float(spacing), float(origin[0]), float(origin[1]),
+                                  float(origin[2]), float(bin_size), float(cutoff_radius),
+                                  int(capacity), slots.reshape(-1, 4), starts, over)
+    if n_over < 0:
+        raise ValueError("invalid bin geometry or capacity")
+    return slots, starts, over[:n_over].copy()
 
 
 def extrema(V):

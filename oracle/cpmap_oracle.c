@@ -35,22 +35,30 @@
  *       fp64 from the fp32 inputs.
  *   R4  the tolerance scale returned beside V is S = sum |q|/r over the atoms
  *       the sum keeps.
- *   R6  the hard-truncated cutoff (the notes' section 18.5 listing: q/r added
- *       only when r2 < rcut2) decides inclusion in fp32, exactly as the GPU
- *       kernel forms r2: dx, dy, dz = fl32(node - atom), r2 = fma(dx, dx,
- *       fma(dy, dy, fl32(dz*dz))), kept iff r2 < fl32(rc*rc).  The kept terms
- *       are summed in fp64.  (An inclusion decision is integer work, so both
- *       sides take it in the same precision.)
- *   R7  ion placement (the notes' section 18.1: positive ions go where the
- *       potential is lowest, negative ions where it is highest): the extrema
- *       of V over its non-NaN nodes; among equal values the smallest node
- *       index; -1 when every node is NaN.
  *   R5  binning: halo H = ceil(rc/bs) bins on each side of the lattice; bin
  *       grid origin b0 = fl(o - H*bs) per axis; atom bin coordinate
  *       t = fl(fl(p - b0) / bs) in fp32; the atom is kept iff 0 <= t < nb on
  *       every axis, and then sits in bin floor(t).  nb per axis = (bin of the
  *       last lattice node) + 1 + H.  Bins are linear x-fastest; atoms sorted
  *       stably by bin (input order inside a bin).
+ *   R14 the hard-truncated cutoff (the notes' section 18.5 listing: q/r added
+ *       only when r2 < rcut2) decides inclusion in fp32, exactly as the GPU
+ *       kernel forms r2: dx, dy, dz = fl32(node - atom), r2 = fma(dx, dx,
+ *       fma(dy, dy, fl32(dz*dz))), kept iff r2 < fl32(rc*rc).  The kept terms
+ *       are summed in fp64.  (An inclusion decision is integer work, so both
+ *       sides take it in the same precision.)
+ *   R15 ion placement (the notes' section 18.1: positive ions go where the
+ *       potential is lowest, negative ions where it is highest): the extrema
+ *       of V over its non-NaN nodes; among equal values the smallest node
+ *       index; -1 when every node is NaN.
+ *   R16 fixed-capacity bins ("Input Binning Lecture Chapter 2", slides 33-35:
+ *       bins of 8 atom slots, 128 bytes, the atoms that do not fit go to an
+ *       extra list): atoms are appended to their bin's slots in input order
+ *       until the slots are full; the later atoms of that bin form its
+ *       overflow, and the overflow list is kept grouped by bin (input order
+ *       inside a bin).  An empty slot holds (+inf, +inf, +inf, 0): a slot is
+ *       recognised as empty by its position, never by a zero charge, because
+ *       a real atom may be neutral.
  *
  * Pins: tests/test_oracle_pins.py checks these functions against closed forms,
  * hand-derived values and invariants.
@@ -202,7 +210,7 @@ void oracle_cutoff(const float *atoms, int64_t n_atoms,
     }
 }
 
-/* Inclusion test of the hard-truncated cutoff (reading R6), all fp32. */
+/* Inclusion test of the hard-truncated cutoff (reading R14), all fp32. */
 static int hard_keep(float x, float y, float z, const float *a, float rc2f)
 {
     const float dx = x - a[0];
@@ -214,7 +222,7 @@ static int hard_keep(float x, float y, float z, const float *a, float rc2f)
 }
 
 /*
- * Hard-truncated cutoff sum (the notes' section 18.5 listing; reading R6):
+ * Hard-truncated cutoff sum (the notes' section 18.5 listing; reading R14):
  * V = sum of q/r over the atoms the fp32 test keeps, r and the sum in fp64.
  * S receives sum |q|/r over the same atoms.
  */
@@ -298,6 +306,20 @@ int32_t oracle_bin_grid(int32_t nx, int32_t ny, int32_t nz, float h,
     return halo;
 }
 
+/* Linear x-fastest bin of one atom (R5), or -1 when it lies outside the grid. */
+static int32_t atom_bin(const float *atom, const int32_t dims[3], const float b0[3],
+                        float bin_size)
+{
+    int32_t c[3];
+    for (int d = 0; d < 3; ++d) {
+        const float t = bin_coord(atom[d], b0[d], bin_size);
+        if (!(t >= 0.0f && t < (float)dims[d]))
+            return -1;
+        c[d] = (int32_t)floorf(t);
+    }
+    return (int32_t)(((int64_t)c[2] * dims[1] + c[1]) * dims[0] + c[0]);
+}
+
 /*
  * Stable counting sort of atoms into the bin grid (R5; slide 28's
  * "bin[position / BIN_SIZE] += atom", kept in input order inside a bin).
@@ -324,18 +346,8 @@ int64_t oracle_bin_atoms(const float *atoms, int64_t n_atoms,
         return -1;
     memset(bin_start, 0, sizeof(int32_t) * (size_t)(nbins + 1));
     for (int64_t a = 0; a < n_atoms; ++a) {
-        int32_t c[3];
-        int keep = 1;
-        for (int d = 0; d < 3; ++d) {
-            const float t = bin_coord(atoms[4 * a + d], b0[d], bin_size);
-            if (!(t >= 0.0f && t < (float)dims[d])) {
-                keep = 0;
-                break;
-            }
-            c[d] = (int32_t)floorf(t);
-        }
-        ids[a] = keep ? (int32_t)(((int64_t)c[2] * dims[1] + c[1]) * dims[0] + c[0]) : -1;
-        if (keep)
+        ids[a] = atom_bin(&atoms[4 * a], dims, b0, bin_size);
+        if (ids[a] >= 0)
             bin_start[ids[a] + 1] += 1;
     }
     for (int64_t b = 0; b < nbins; ++b)
@@ -359,7 +371,75 @@ int64_t oracle_bin_atoms(const float *atoms, int64_t n_atoms,
 }
 
 /*
- * Extrema of a potential map for ion placement (reading R7).  out_index[0] =
+ * Fixed-capacity bins with an overflow list (R16).
+ *   slots       nbins*capacity x 4 floats: slot s of bin b is row
+ *               b*capacity + s; empty slots hold (+inf, +inf, +inf, 0).
+ *   over_start  nbins+1 int32: the overflow atoms of bin b are rows
+ *               over_start[b] .. over_start[b+1]-1 of over_atoms.
+ *   over_atoms  n_atoms x 4 floats (only the first over_start[nbins] rows
+ *               are written).
+ * Atoms outside the bin grid are dropped, as in oracle_bin_atoms.  Returns
+ * the number of overflow atoms, or -1 on invalid arguments.
+ */
+int64_t oracle_bin_slots(const float *atoms, int64_t n_atoms,
+                         int32_t nx, int32_t ny, int32_t nz, float h,
+                         float ox, float oy, float oz,
+                         float bin_size, float cutoff, int32_t capacity,
+                         float *slots, int32_t *over_start, float *over_atoms)
+{
+    int32_t dims[3];
+    float b0[3];
+    if (capacity < 1 ||
+        oracle_bin_grid(nx, ny, nz, h, ox, oy, oz, bin_size, cutoff, dims, b0) < 0)
+        return -1;
+    const int64_t nbins = (int64_t)dims[0] * dims[1] * dims[2];
+    int32_t *fill = (int32_t *)calloc((size_t)nbins, sizeof(int32_t));
+    int32_t *over_bin = (int32_t *)malloc(sizeof(int32_t) * (size_t)(n_atoms > 0 ? n_atoms : 1));
+    if (!fill || !over_bin) {
+        free(fill);
+        free(over_bin);
+        return -1;
+    }
+    for (int64_t e = 0; e < nbins * capacity; ++e) {
+        slots[4 * e + 0] = INFINITY;
+        slots[4 * e + 1] = INFINITY;
+        slots[4 * e + 2] = INFINITY;
+        slots[4 * e + 3] = 0.0f;
+    }
+    memset(over_start, 0, sizeof(int32_t) * (size_t)(nbins + 1));
+    /* the sequential fill: each atom takes the next free slot of its bin */
+    for (int64_t a = 0; a < n_atoms; ++a) {
+        over_bin[a] = -1;
+        const int32_t b = atom_bin(&atoms[4 * a], dims, b0, bin_size);
+        if (b < 0)
+            continue;
+        if (fill[b] < capacity) {
+            memcpy(&slots[4 * ((int64_t)b * capacity + fill[b])], &atoms[4 * a],
+                   4 * sizeof(float));
+            fill[b] += 1;
+        } else {
+            over_bin[a] = b;
+            over_start[b + 1] += 1;
+        }
+    }
+    /* group the overflow list by bin, input order inside a bin */
+    for (int64_t b = 0; b < nbins; ++b)
+        over_start[b + 1] += over_start[b];
+    memset(fill, 0, sizeof(int32_t) * (size_t)nbins);
+    for (int64_t a = 0; a < n_atoms; ++a) {
+        const int32_t b = over_bin[a];
+        if (b < 0)
+            continue;
+        const int64_t dst = (int64_t)over_start[b] + fill[b]++;
+        memcpy(&over_atoms[4 * dst], &atoms[4 * a], 4 * sizeof(float));
+    }
+    free(fill);
+    free(over_bin);
+    return over_start[nbins];
+}
+
+/*
+ * Extrema of a potential map for ion placement (reading R15).  out_index[0] =
  * argmin, out_index[1] = argmax (smallest index among equal values, NaN
  * nodes skipped, -1 when there is no non-NaN node); out_value[0..1] = the
  * values at those nodes (NaN when the index is -1).

@@ -321,6 +321,71 @@ def test_bin_atoms_is_a_stable_sort_with_correct_boxes():
     assert (~kept).sum() > 0 and kept.sum() > 0
 
 
+def _step(points, n):
+    """Expand {index: value} breakpoints into a step function over 0..n-1."""
+    keys = sorted(int(k) for k in points)
+    out, v, it = [], None, 0
+    for i in range(n):
+        while it < len(keys) and keys[it] <= i:
+            v = points[str(keys[it])]
+            it += 1
+        out.append(v)
+    return out
+
+
+def _is_empty_slot(rows):
+    return np.isposinf(rows[:, 0]) & np.isposinf(rows[:, 1]) & np.isposinf(rows[:, 2]) & (rows[:, 3] == 0)
+
+
+def test_bin_slots_golden(golden_dir):
+    """Fixed-capacity bins (the binning lecture's slides 33-35) on hand-worked
+    atoms: first-come slots, the overflow list grouped by bin, a neutral atom
+    kept in a slot, atoms on bin faces, dropped atoms; capacities 1, 3, 8."""
+    with open(os.path.join(golden_dir, "bin_slots.json")) as f:
+        fx = json.load(f)
+    L = fx["lattice"]
+    atoms = np.array(fx["atoms"], dtype=np.float32)
+    for case in fx["cases"]:
+        cap = case["capacity"]
+        slots, starts, over = oracle.bin_slots(atoms, L["dims"], L["spacing"], L["origin"],
+                                               L["bin_size"], L["cutoff"], cap)
+        assert slots.shape == (64, cap, 4)
+        for b in range(64):
+            want = case["slots"].get(str(b), [])
+            np.testing.assert_array_equal(slots[b, :len(want)], atoms[want], err_msg=f"bin {b}")
+            assert _is_empty_slot(slots[b, len(want):]).all(), f"bin {b} cap {cap}"
+        np.testing.assert_array_equal(over, atoms[case["overflow"]].reshape(-1, 4))
+        assert list(starts) == _step(case["over_start"], 65), f"cap {cap}"
+
+
+@pytest.mark.parametrize("cap", [1, 5, 8, 64])
+def test_bin_slots_splits_the_stable_sort(cap):
+    """Each bin's filled slots followed by its overflow atoms are exactly the
+    bin's atoms in input order (the stable sort, pinned above); slots fill
+    from the front; a bin keeps min(count, capacity) atoms in its slots;
+    neutral atoms are never taken for empty slots."""
+    dims, h, o, bs, rc = (24, 20, 16), 0.5, (0.5, -1.0, 2.0), 2.0, 4.0
+    A = random_atoms(6000, (-3, -4, -1), (14, 10, 12), seed=83)
+    A[::7, 3] = 0.0
+    slots, ostart, over = oracle.bin_slots(A, dims, h, o, bs, rc, cap)
+    starts, srt, _ = oracle.bin_atoms(A, dims, h, o, bs, rc)
+    nb = starts.size - 1
+    assert slots.shape == (nb, cap, 4) and ostart.size == nb + 1
+    cnt = np.diff(starts)
+    assert cnt.max() > 1
+    np.testing.assert_array_equal(np.diff(ostart), np.maximum(cnt - cap, 0))
+    assert ostart[0] == 0 and over.shape[0] == ostart[-1]
+    for b in np.nonzero(cnt)[0]:
+        k = min(cnt[b], cap)
+        got = np.concatenate([slots[b, :k], over[ostart[b]:ostart[b + 1]]])
+        np.testing.assert_array_equal(got, srt[starts[b]:starts[b + 1]])
+        assert not _is_empty_slot(slots[b, :k]).any()
+        assert _is_empty_slot(slots[b, k:]).all()
+    assert _is_empty_slot(slots[cnt == 0].reshape(-1, 4)).all()
+    if cap >= cnt.max():
+        assert over.shape[0] == 0
+
+
 # ---------------------------------------------------------------- hard-truncated cutoff
 
 def test_cutoff_hard_single_atom_values_and_tie():
@@ -333,7 +398,7 @@ def test_cutoff_hard_single_atom_values_and_tie():
 
 
 def test_cutoff_hard_decision_is_taken_in_fp32():
-    """Reading R6: an atom one fp32 ulp inside rc along x is kept (its fp32
+    """Reading R14: an atom one fp32 ulp inside rc along x is kept (its fp32
     r^2 rounds below 144), one ulp outside is not; the kept value is q/r with
     r the exact fp64 distance."""
     inside = np.nextafter(np.float32(12.0), np.float32(0.0))
@@ -378,7 +443,7 @@ def _golden_values(vals):
 
 
 def test_extrema_golden(golden_dir):
-    """Hand-worked argmin/argmax with ties, NaN, +-inf and +-0 (reading R7)."""
+    """Hand-worked argmin/argmax with ties, NaN, +-inf and +-0 (reading R15)."""
     with open(os.path.join(golden_dir, "extrema.json")) as f:
         fx = json.load(f)
     for case in fx["cases"]:
