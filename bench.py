@@ -286,6 +286,7 @@ def bench_cutoff(torch, cpmap, wl, dev, args):
     bytes_alg = 16 * w.n_atoms + 4 * lat.n_points
     return {
         "workload": w.name,
+        "fixed_slots": bench_slots(torch, cpmap, w, ws, V, cut_ms, steps, args),
         "bin_ms_median": bin_ms,
         "cutoff_ms_median": cut_ms,
         "cutoff_ms_min": min(per_cut),
@@ -297,6 +298,34 @@ def bench_cutoff(torch, cpmap, wl, dev, args):
         "hbm_traffic_bytes_per_launch": measured_traffic(
             "cutoff_kernel_200cube_100k_rc12.md", "direct_coulomb_potential_amd/csrc/cutoff.hip"),
         "direct_equivalent_G_evals_per_s": w.pairs / ((cut_ms + bin_ms) * 1e-3) / 1e9,
+    }
+
+
+def bench_slots(torch, cpmap, w, ws, V, csr_cut_ms, steps, args, cap=8):
+    """Fixed-capacity bins (8 slots per bin, the binning lecture's layout)
+    with a GPU overflow pass, timed beside the CSR cutoff on the same atoms."""
+    lat, bs, rc = w.lattice, w.bin_size, w.cutoff
+    try:
+        sws = cpmap.bin_slots(ws, w.n_atoms, lat, bs, rc, cap)
+        cpmap.cutoff_slots(sws, w.n_atoms, lat, bs, rc, cap, out=V)
+        torch.cuda.synchronize()
+    except cpmap.CpmapError as e:
+        return {"skipped": str(e)}
+    n_over = int(cpmap.slot_views(sws, w.n_atoms, lat, bs, rc, cap)[1][-1].item())
+    _, per_fill = time_launches(
+        torch, lambda: cpmap.bin_slots(ws, w.n_atoms, lat, bs, rc, cap, slot_workspace=sws),
+        steps, args.warmup)
+    _, per_cut = time_launches(
+        torch, lambda: cpmap.cutoff_slots(sws, w.n_atoms, lat, bs, rc, cap, out=V),
+        steps, args.warmup)
+    cut_ms = statistics.median(per_cut)
+    return {
+        "capacity": cap,
+        "overflow_atoms": n_over,
+        "overflow_fraction": n_over / max(w.n_atoms, 1),
+        "bin_slots_ms_median": statistics.median(per_fill),
+        "cutoff_slots_ms_median": cut_ms,
+        "vs_csr_cutoff": cut_ms / csr_cut_ms,
     }
 
 

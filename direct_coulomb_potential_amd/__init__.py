@@ -25,6 +25,7 @@ __all__ = [
     "Lattice", "CpmapError", "direct", "direct_scatter", "direct_workspace_bytes", "direct_plan", "bin_atoms", "cutoff", "bin_workspace_bytes",
     "bin_grid", "workspace_layout", "workspace_views", "neighbor_spans", "library",
     "library_path", "header_functions", "STATUS", "extrema", "place_ions", "TERMS",
+    "slot_workspace_bytes", "slot_layout", "bin_slots", "slot_views", "cutoff_slots",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -67,6 +68,11 @@ _SIGNATURES = {
     "cpmap_extrema": (_i32, [_vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "cpmap_neighbor_spans": (_i64, [*_LAT, _f32, _f32, _i32, _i32, _i32, ctypes.POINTER(_i32),
                                     _i64]),
+    "cpmap_slot_workspace_bytes": (_sz, [_i64, *_LAT, _f32, _f32, _i32]),
+    "cpmap_slot_layout": (_i32, [_i64, *_LAT, _f32, _f32, _i32, ctypes.POINTER(_i64),
+                                 ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
+    "cpmap_bin_slots": (_i32, [_vp, _sz, _i64, *_LAT, _f32, _f32, _i32, _vp, _sz, _vp]),
+    "cpmap_cutoff_slots": (_i32, [_vp, _sz, _i64, *_LAT, _f32, _f32, _i32, _i32, _vp, _vp]),
 }
 
 
@@ -271,6 +277,71 @@ def cutoff(workspace, n_atoms: int, lat: Lattice, bin_size: float, cutoff: float
                                      *_lat_args(lat), float(bin_size), float(cutoff),
                                      TERMS[term], V.data_ptr(), _stream_ptr(workspace.device))
     _check("cpmap_cutoff_term", st)
+    return V
+
+
+def slot_workspace_bytes(n_atoms: int, lat: Lattice, bin_size: float, cutoff: float,
+                         capacity: int = 8) -> int:
+    n = library().cpmap_slot_workspace_bytes(int(n_atoms), *_lat_args(lat), float(bin_size),
+                                             float(cutoff), int(capacity))
+    if n == 0:
+        raise CpmapError("cpmap_slot_workspace_bytes", 1, "invalid geometry or capacity")
+    return int(n)
+
+
+def slot_layout(n_atoms: int, lat: Lattice, bin_size: float, cutoff: float, capacity: int = 8):
+    a, b, c = _i64(), _i64(), _i64()
+    _check("cpmap_slot_layout",
+           library().cpmap_slot_layout(int(n_atoms), *_lat_args(lat), float(bin_size),
+                                       float(cutoff), int(capacity), ctypes.byref(a),
+                                       ctypes.byref(b), ctypes.byref(c)))
+    return int(a.value), int(b.value), int(c.value)
+
+
+def bin_slots(workspace, n_atoms: int, lat: Lattice, bin_size: float, cutoff: float,
+              capacity: int = 8, slot_workspace=None):
+    """Fixed-capacity bins (capacity slots per bin plus an overflow list) from a
+    workspace that bin_atoms filled; returns the slot workspace (uint8 tensor)."""
+    torch = _torch()
+    need = slot_workspace_bytes(n_atoms, lat, bin_size, cutoff, capacity)
+    if slot_workspace is None:
+        slot_workspace = torch.empty(need, dtype=torch.uint8, device=workspace.device)
+    if slot_workspace.dtype != torch.uint8 or not slot_workspace.is_cuda \
+            or not slot_workspace.is_contiguous():
+        raise ValueError("slot_workspace must be a contiguous uint8 GPU tensor")
+    st = library().cpmap_bin_slots(workspace.data_ptr(), workspace.numel(), int(n_atoms),
+                                   *_lat_args(lat), float(bin_size), float(cutoff),
+                                   int(capacity), slot_workspace.data_ptr(),
+                                   slot_workspace.numel(), _stream_ptr(workspace.device))
+    _check("cpmap_bin_slots", st)
+    return slot_workspace
+
+
+def slot_views(slot_workspace, n_atoms: int, lat: Lattice, bin_size: float, cutoff: float,
+               capacity: int = 8):
+    """(slots float32[nbins, capacity, 4], over_start int32[nbins+1],
+    over_atoms float32[n_atoms, 4]) views into a slot workspace."""
+    torch = _torch()
+    s_off, o_off, a_off = slot_layout(n_atoms, lat, bin_size, cutoff, capacity)
+    bx, by, bz = bin_grid(lat, bin_size, cutoff)
+    nb = bx * by * bz
+    slots = slot_workspace[s_off:s_off + 16 * nb * capacity].view(torch.float32)
+    starts = slot_workspace[o_off:o_off + 4 * (nb + 1)].view(torch.int32)
+    over = slot_workspace[a_off:a_off + 16 * n_atoms].view(torch.float32)
+    return slots.view(nb, capacity, 4), starts, over.view(n_atoms, 4)
+
+
+def cutoff_slots(slot_workspace, n_atoms: int, lat: Lattice, bin_size: float, cutoff: float,
+                 capacity: int = 8, out=None, term: str = "smoothed"):
+    """The cutoff sum over fixed-capacity bins (slot pass, then overflow pass)."""
+    if term not in TERMS:
+        raise ValueError(f"term must be one of {sorted(TERMS)}")
+    V = _out(lat, slot_workspace.device, out)
+    st = library().cpmap_cutoff_slots(slot_workspace.data_ptr(), slot_workspace.numel(),
+                                      int(n_atoms), *_lat_args(lat), float(bin_size),
+                                      float(cutoff), int(capacity), TERMS[term], V.data_ptr(),
+                                      _stream_ptr(slot_workspace.device))
+    _check("cpmap_cutoff_slots", st)
     return V
 
 

@@ -31,21 +31,23 @@ cpmap_status check_lattice(int32_t nx, int32_t ny, int32_t nz, float h, float ox
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Host-side record of the geometry each workspace was binned for, so that
-// cpmap_cutoff can reject a workspace binned for something else without
-// reading device memory.
+// Host-side record of the geometry each workspace was binned for (and the
+// slot capacity, for slot workspaces), so that the cutoff entry points can
+// reject a workspace filled for something else without reading device memory.
 struct WorkspaceKey {
     int64_t n_atoms;
     int32_t n[3];
     float h, o[3], bs, rc;
+    int32_t cap;
     bool operator==(const WorkspaceKey &k) const { return std::memcmp(this, &k, sizeof k) == 0; }
 };
 
 std::mutex g_mu;
-std::unordered_map<const void *, WorkspaceKey> g_binned;
+std::unordered_map<const void *, WorkspaceKey> g_binned;  // CSR workspaces
+std::unordered_map<const void *, WorkspaceKey> g_slotted; // slot workspaces
 
 WorkspaceKey make_key(int64_t n_atoms, int32_t nx, int32_t ny, int32_t nz, float h, float ox,
-                      float oy, float oz, float bs, float rc)
+                      float oy, float oz, float bs, float rc, int32_t cap = 0)
 {
     WorkspaceKey k;
     std::memset(&k, 0, sizeof k);  // padding bytes take part in operator==
@@ -59,6 +61,7 @@ WorkspaceKey make_key(int64_t n_atoms, int32_t nx, int32_t ny, int32_t nz, float
     k.o[2] = oz;
     k.bs = bs;
     k.rc = rc;
+    k.cap = cap;
     return k;
 }
 
@@ -92,6 +95,17 @@ cpmap_status axis_bins(int32_t n, float h, float o, float bs, int32_t halo, Axis
     return CPMAP_OK;
 }
 
+// Geometry and slot layout for the fixed-capacity entry points.
+cpmap_status slot_setup(int64_t n_atoms, int32_t nx, int32_t ny, int32_t nz, float h, float ox,
+                        float oy, float oz, float bs, float rc, int32_t cap, BinGeometry *g,
+                        SlotLayout *S);
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb)
+{
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
 }  // namespace
 
 cpmap_status make_bin_geometry(int32_t nx, int32_t ny, int32_t nz, float h, float ox, float oy,
@@ -121,6 +135,27 @@ cpmap_status make_bin_geometry(int32_t nx, int32_t ny, int32_t nz, float h, floa
         return CPMAP_ERANGE;
     return CPMAP_OK;
 }
+
+namespace {
+
+cpmap_status slot_setup(int64_t n_atoms, int32_t nx, int32_t ny, int32_t nz, float h, float ox,
+                        float oy, float oz, float bs, float rc, int32_t cap, BinGeometry *g,
+                        SlotLayout *S)
+{
+    if (n_atoms < 0 || cap < 1 || cap > CPMAP_MAX_SLOTS)
+        return CPMAP_EINVAL;
+    if (n_atoms > CPMAP_MAX_ATOMS)
+        return CPMAP_ERANGE;
+    cpmap_status st = make_bin_geometry(nx, ny, nz, h, ox, oy, oz, bs, rc, g);
+    if (st != CPMAP_OK)
+        return st;
+    if (g->nbins() * cap >= (int64_t)INT32_MAX)
+        return CPMAP_ERANGE;
+    *S = slot_layout(n_atoms, *g, cap);
+    return CPMAP_OK;
+}
+
+}  // namespace
 
 }  // namespace cpmap
 
@@ -302,6 +337,7 @@ cpmap_status cpmap_bin_atoms(const float *atoms, int64_t n_atoms, int32_t nx, in
     {
         std::lock_guard<std::mutex> lock(g_mu);
         g_binned.erase(workspace);
+        g_slotted.erase(workspace);
     }
     hipError_t e = launch_bin_atoms(reinterpret_cast<const float4 *>(atoms), n_atoms, lat, g, L,
                                     workspace, static_cast<hipStream_t>(stream));
@@ -353,6 +389,115 @@ cpmap_status cpmap_cutoff(const void *workspace, size_t workspace_bytes, int64_t
 {
     return cpmap_cutoff_term(workspace, workspace_bytes, n_atoms, nx, ny, nz, spacing, ox, oy, oz,
                              bin_size, cutoff, CPMAP_TERM_SMOOTHED, V, stream);
+}
+
+size_t cpmap_slot_workspace_bytes(int64_t n_atoms, int32_t nx, int32_t ny, int32_t nz,
+                                  float spacing, float ox, float oy, float oz, float bin_size,
+                                  float cutoff, int32_t capacity)
+{
+    BinGeometry g;
+    SlotLayout S;
+    if (slot_setup(n_atoms, nx, ny, nz, spacing, ox, oy, oz, bin_size, cutoff, capacity, &g, &S) !=
+        CPMAP_OK)
+        return 0;
+    return S.total;
+}
+
+cpmap_status cpmap_slot_layout(int64_t n_atoms, int32_t nx, int32_t ny, int32_t nz,
+                               float spacing, float ox, float oy, float oz, float bin_size,
+                               float cutoff, int32_t capacity, int64_t *slots_offset,
+                               int64_t *over_start_offset, int64_t *over_atoms_offset)
+{
+    int64_t *outs[3] = {slots_offset, over_start_offset, over_atoms_offset};
+    for (int64_t *o : outs)
+        if (o)
+            *o = -1;
+    for (int64_t *o : outs)
+        if (o == nullptr)
+            return CPMAP_EINVAL;
+    BinGeometry g;
+    SlotLayout S;
+    cpmap_status st =
+        slot_setup(n_atoms, nx, ny, nz, spacing, ox, oy, oz, bin_size, cutoff, capacity, &g, &S);
+    if (st != CPMAP_OK)
+        return st;
+    *slots_offset = (int64_t)S.slots;
+    *over_start_offset = (int64_t)S.over_start;
+    *over_atoms_offset = (int64_t)S.over_atoms;
+    return CPMAP_OK;
+}
+
+cpmap_status cpmap_bin_slots(const void *workspace, size_t workspace_bytes, int64_t n_atoms,
+                             int32_t nx, int32_t ny, int32_t nz, float spacing, float ox,
+                             float oy, float oz, float bin_size, float cutoff, int32_t capacity,
+                             void *slot_workspace, size_t slot_workspace_bytes, void *stream)
+{
+    BinGeometry g;
+    SlotLayout S;
+    cpmap_status st =
+        slot_setup(n_atoms, nx, ny, nz, spacing, ox, oy, oz, bin_size, cutoff, capacity, &g, &S);
+    if (st != CPMAP_OK)
+        return st;
+    if (workspace == nullptr || slot_workspace == nullptr)
+        return CPMAP_EINVAL;
+    if (!aligned(workspace, 256) || !aligned(slot_workspace, 256))
+        return CPMAP_EINVAL;
+    const BinLayout L = bin_layout(n_atoms, g);
+    if (workspace_bytes < L.total || slot_workspace_bytes < S.total)
+        return CPMAP_ENOSPC;
+    if (overlaps(workspace, L.total, slot_workspace, S.total))
+        return CPMAP_EINVAL;
+    {
+        std::lock_guard<std::mutex> lock(g_mu);
+        auto it = g_binned.find(workspace);
+        if (it == g_binned.end() ||
+            !(it->second == make_key(n_atoms, nx, ny, nz, spacing, ox, oy, oz, bin_size, cutoff)))
+            return CPMAP_EGEOM;
+        g_slotted.erase(slot_workspace);
+        g_binned.erase(slot_workspace);
+    }
+    hipError_t e = launch_bin_slots(workspace, L, n_atoms, g, capacity, slot_workspace, S,
+                                    static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return CPMAP_EHIP;
+    std::lock_guard<std::mutex> lock(g_mu);
+    g_slotted[slot_workspace] =
+        make_key(n_atoms, nx, ny, nz, spacing, ox, oy, oz, bin_size, cutoff, capacity);
+    return CPMAP_OK;
+}
+
+cpmap_status cpmap_cutoff_slots(const void *slot_workspace, size_t slot_workspace_bytes,
+                                int64_t n_atoms, int32_t nx, int32_t ny, int32_t nz,
+                                float spacing, float ox, float oy, float oz, float bin_size,
+                                float cutoff, int32_t capacity, int32_t term, float *V,
+                                void *stream)
+{
+    if (term != CPMAP_TERM_SMOOTHED && term != CPMAP_TERM_TRUNCATED)
+        return CPMAP_EINVAL;
+    BinGeometry g;
+    SlotLayout S;
+    cpmap_status st =
+        slot_setup(n_atoms, nx, ny, nz, spacing, ox, oy, oz, bin_size, cutoff, capacity, &g, &S);
+    if (st != CPMAP_OK)
+        return st;
+    if (slot_workspace == nullptr || V == nullptr)
+        return CPMAP_EINVAL;
+    if (!aligned(slot_workspace, 256) || !aligned(V, 4))
+        return CPMAP_EINVAL;
+    if (slot_workspace_bytes < S.total)
+        return CPMAP_ENOSPC;
+    {
+        std::lock_guard<std::mutex> lock(g_mu);
+        auto it = g_slotted.find(slot_workspace);
+        if (it == g_slotted.end() ||
+            !(it->second ==
+              make_key(n_atoms, nx, ny, nz, spacing, ox, oy, oz, bin_size, cutoff, capacity)))
+            return CPMAP_EGEOM;
+    }
+    const Lattice lat = make_lattice(nx, ny, nz, spacing, ox, oy, oz);
+    hipError_t e = launch_cutoff_slots(slot_workspace, S, n_atoms, lat, g, capacity, term, V,
+                                       static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? CPMAP_OK : CPMAP_EHIP;
 }
 
 cpmap_status cpmap_direct_scatter(const float *atoms, int64_t n_atoms, int32_t nx, int32_t ny,

@@ -86,6 +86,28 @@ hipError_t launch_cutoff(const void *workspace, const BinLayout &L, int64_t n_at
                          const Lattice &lat, const BinGeometry &g, int32_t term, float *V,
                          hipStream_t stream);
 
+// Fixed-capacity bins: cap slots per bin plus an overflow list in CSR form,
+// both derived from the stable CSR of a binned workspace.
+struct SlotLayout {
+    size_t slots;       // float4[nbins * cap]
+    size_t over_start;  // int32[nbins + 1]
+    size_t over_atoms;  // float4[n_atoms]
+    size_t chunk_sum;   // int32[n_chunks + 1] (overflow counts per chunk of bins)
+    size_t total;
+    int64_t n_chunks;
+};
+
+SlotLayout slot_layout(int64_t n_atoms, const BinGeometry &g, int32_t cap);
+
+hipError_t launch_bin_slots(const void *bin_workspace, const BinLayout &L, int64_t n_atoms,
+                            const BinGeometry &g, int32_t cap, void *slot_workspace,
+                            const SlotLayout &S, hipStream_t stream);
+
+// The slot pass, then the overflow pass adding into V.
+hipError_t launch_cutoff_slots(const void *slot_workspace, const SlotLayout &S, int64_t n_atoms,
+                               const Lattice &lat, const BinGeometry &g, int32_t cap,
+                               int32_t term, float *V, hipStream_t stream);
+
 // Scatter form of the direct sum (atomics; a measured contrast).
 hipError_t launch_scatter(const float4 *atoms, int64_t n_atoms, const Lattice &lat, float *V,
                           hipStream_t stream);

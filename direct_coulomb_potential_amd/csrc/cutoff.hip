@@ -33,6 +33,12 @@
 //    q -> 0 is the fallback), so atoms beyond the cutoff add exactly nothing
 //    and nodes beyond rc of every atom get exactly 0;
 //  - V is written once per node, x-fastest.
+//
+// The same kernel walks fixed-capacity bins (the lecture's slides 33-35): a
+// run of bins is then a run of cap-slot blocks, whose span follows from the
+// geometry alone, and empty slots (at +inf) never pass the per-wave list
+// test.  The bins' overflow is a CSR of its own; a second launch walks it and
+// adds into V, skipping tiles whose neighbourhood holds no overflow atom.
 #include <cmath>
 
 #include "cpmap_internal.h"
@@ -173,6 +179,7 @@ struct CutoffParams {
     float list_rc;  // radius of the bin neighbourhood (rc, widened for the truncated term)
     float gc0, gc1, gc2;
     int32_t truncated;
+    int32_t cap;  // slots per bin (fixed-capacity source)
 };
 
 constexpr int kWaves = kThreads / 64;
@@ -254,6 +261,10 @@ __device__ __forceinline__ void sweep(const float4 *stage, const uint16_t *list,
         add_atom<MODE>(stage[list[i]], x, y, z, P, acc);
 }
 
+// SLOTS = false: the atoms are a CSR (bin_start, sorted); SLOTS = true: they
+// are fixed-capacity bins, bin b's slots at sorted[b * cap ...], and
+// bin_start is not read.  ACCUM = true adds the sum into V.
+template <bool SLOTS, bool ACCUM>
 __global__ __launch_bounds__(kThreads) void cutoff_kernel(CutoffParams P0,
                                                           const int32_t *__restrict__ bin_start,
                                                           const float4 *__restrict__ sorted,
@@ -317,6 +328,7 @@ __global__ __launch_bounds__(kThreads) void cutoff_kernel(CutoffParams P0,
                                      P.o[2])};
     // a slightly widened radius keeps the list conservative against rounding
     const float keep2 = P0.rc2 * 1.0001f;
+    bool any_atoms = false;
 
     for (int32_t row0 = 0; row0 < T.nrows; row0 += kMaxRows) {
         const int32_t rows = T.nrows - row0 < kMaxRows ? T.nrows - row0 : kMaxRows;
@@ -329,12 +341,17 @@ __global__ __launch_bounds__(kThreads) void cutoff_kernel(CutoffParams P0,
             int32_t cy, cz, cx0, cx1, cnt = 0, src = 0;
             if (tile_row(T, row0 + r, P.b0, P.nb, P.bs, P.list_rc, &cy, &cz, &cx0, &cx1)) {
                 const int64_t base = ((int64_t)cz * P.nb[1] + cy) * P.nb[0];
-                int32_t s = bin_start[base + cx0];
-                int32_t e = bin_start[base + cx1 + 1];
-                s = s < 0 ? 0 : (s > n_sorted ? n_sorted : s);
-                e = e < s ? s : (e > n_sorted ? n_sorted : e);
-                src = s;
-                cnt = e - s;
+                if constexpr (SLOTS) {
+                    src = (int32_t)((base + cx0) * P.cap);
+                    cnt = (cx1 - cx0 + 1) * P.cap;
+                } else {
+                    int32_t s = bin_start[base + cx0];
+                    int32_t e = bin_start[base + cx1 + 1];
+                    s = s < 0 ? 0 : (s > n_sorted ? n_sorted : s);
+                    e = e < s ? s : (e > n_sorted ? n_sorted : e);
+                    src = s;
+                    cnt = e - s;
+                }
             }
             span_src[r] = src;
             span_off[r] = cnt;
@@ -358,6 +375,7 @@ __global__ __launch_bounds__(kThreads) void cutoff_kernel(CutoffParams P0,
         const int32_t total = __builtin_amdgcn_readfirstlane(scan_tmp[kThreads - 1]);
         if (t == 0)
             span_off[rows] = total;
+        any_atoms |= total > 0;
         __syncthreads();
 
         // 3. stage the spans' atoms in chunks; each wave lists the atoms near
@@ -413,6 +431,16 @@ __global__ __launch_bounds__(kThreads) void cutoff_kernel(CutoffParams P0,
     if (j >= P.n[1] || k >= P.n[2])
         return;
     float *out = V + ((int64_t)k * P.n[1] + j) * P.n[0];
+    if constexpr (ACCUM) {
+        // nothing within reach of this tile: its nodes keep their value
+        if (!any_atoms)
+            return;
+#pragma unroll
+        for (int c = 0; c < kNx; ++c)
+            if (i0 + c < P.n[0])
+                out[i0 + c] += acc[c];
+        return;
+    }
 #pragma unroll
     for (int c = 0; c < kNx; ++c)
         if (i0 + c < P.n[0])
@@ -421,11 +449,8 @@ __global__ __launch_bounds__(kThreads) void cutoff_kernel(CutoffParams P0,
 
 int32_t ceil_div32(int32_t a, int32_t b) { return (a + b - 1) / b; }
 
-}  // namespace
 
-hipError_t launch_cutoff(const void *workspace, const BinLayout &L, int64_t n_atoms,
-                         const Lattice &lat, const BinGeometry &g, int32_t term, float *V,
-                         hipStream_t stream)
+CutoffParams make_params(const Lattice &lat, const BinGeometry &g, int32_t term, int32_t cap)
 {
     CutoffParams P;
     P.truncated = term == CPMAP_TERM_TRUNCATED;
@@ -449,7 +474,23 @@ hipError_t launch_cutoff(const void *workspace, const BinLayout &L, int64_t n_at
     P.gc0 = (float)(15.0 / (8.0 * rc));
     P.gc1 = (float)(-5.0 / (4.0 * rc * rc * rc));
     P.gc2 = (float)(3.0 / (8.0 * rc * rc * rc * rc * rc));
-    const int64_t tiles = (int64_t)P.tiles[0] * P.tiles[1] * P.tiles[2];
+    P.cap = cap;
+    return P;
+}
+
+int64_t tile_count(const CutoffParams &P)
+{
+    return (int64_t)P.tiles[0] * P.tiles[1] * P.tiles[2];
+}
+
+}  // namespace
+
+hipError_t launch_cutoff(const void *workspace, const BinLayout &L, int64_t n_atoms,
+                         const Lattice &lat, const BinGeometry &g, int32_t term, float *V,
+                         hipStream_t stream)
+{
+    const CutoffParams P = make_params(lat, g, term, 0);
+    const int64_t tiles = tile_count(P);
     if (tiles == 0)
         return hipSuccess;
     if (tiles > INT32_MAX)
@@ -457,8 +498,31 @@ hipError_t launch_cutoff(const void *workspace, const BinLayout &L, int64_t n_at
     const char *ws = static_cast<const char *>(workspace);
     const int32_t *bin_start = reinterpret_cast<const int32_t *>(ws + L.bin_start);
     const float4 *sorted = reinterpret_cast<const float4 *>(ws + L.sorted);
-    hipLaunchKernelGGL(cutoff_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, stream, P,
-                       bin_start, sorted, (int32_t)n_atoms, V);
+    hipLaunchKernelGGL((cutoff_kernel<false, false>), dim3((unsigned)tiles), dim3(kThreads), 0,
+                       stream, P, bin_start, sorted, (int32_t)n_atoms, V);
+    return hipGetLastError();
+}
+
+hipError_t launch_cutoff_slots(const void *slot_workspace, const SlotLayout &S, int64_t n_atoms,
+                               const Lattice &lat, const BinGeometry &g, int32_t cap,
+                               int32_t term, float *V, hipStream_t stream)
+{
+    const CutoffParams Pslots = make_params(lat, g, term, cap);
+    const CutoffParams Pover = make_params(lat, g, term, 0);
+    const int64_t tiles = tile_count(Pslots);
+    if (tiles == 0)
+        return hipSuccess;
+    if (tiles > INT32_MAX)
+        return hipErrorInvalidValue;
+    const char *ws = static_cast<const char *>(slot_workspace);
+    const float4 *slots = reinterpret_cast<const float4 *>(ws + S.slots);
+    const int32_t *over_start = reinterpret_cast<const int32_t *>(ws + S.over_start);
+    const float4 *over_atoms = reinterpret_cast<const float4 *>(ws + S.over_atoms);
+    const int64_t n_slots = g.nbins() * cap;
+    hipLaunchKernelGGL((cutoff_kernel<true, false>), dim3((unsigned)tiles), dim3(kThreads), 0,
+                       stream, Pslots, nullptr, slots, (int32_t)n_slots, V);
+    hipLaunchKernelGGL((cutoff_kernel<false, true>), dim3((unsigned)tiles), dim3(kThreads), 0,
+                       stream, Pover, over_start, over_atoms, (int32_t)n_atoms, V);
     return hipGetLastError();
 }
 

@@ -288,6 +288,94 @@ int64_t cpmap_neighbor_spans(int32_t nx, int32_t ny, int32_t nz, float spacing,
                              int32_t *spans_out, int64_t max_spans);
 
 /*
+ * Fixed-capacity bins (the binning lecture's slides 33-35: every bin has the
+ * same number of atom slots, 8 slots of 16 bytes there, and the atoms that
+ * do not fit their bin go to an extra list).  They are derived on the GPU from
+ * a workspace binned by cpmap_bin_atoms, so a bin's slots hold its first
+ * `capacity` atoms in input order and its later atoms are its overflow.  An
+ * alternative layout for the cutoff sum, kept for measurement beside the CSR
+ * (which never overflows).
+ *
+ * A slot workspace holds (byte offsets: cpmap_slot_layout):
+ *   slots       float4[nbins * capacity]: slot s of bin b at b*capacity + s;
+ *               an empty slot is (+inf, +inf, +inf, 0).  Empty slots are told
+ *               apart by their position, never by a zero charge, so a neutral
+ *               atom is never taken for one.
+ *   over_start  int32[nbins + 1]: the overflow atoms of bin b are
+ *               over_atoms[over_start[b] .. over_start[b+1]), input order
+ *   over_atoms  float4[n_atoms]; the first over_start[nbins] are written
+ * 1 <= capacity <= CPMAP_MAX_SLOTS, and nbins * capacity < 2^31.
+ */
+#define CPMAP_MAX_SLOTS 256
+
+/*
+ * cpmap_slot_workspace_bytes -- size of a slot workspace for this atom
+ * count, geometry and capacity.  Host only, no HIP call.  Returns 0 when the
+ * arguments are invalid or too large.
+ */
+size_t cpmap_slot_workspace_bytes(int64_t n_atoms,
+                                  int32_t nx, int32_t ny, int32_t nz, float spacing,
+                                  float ox, float oy, float oz,
+                                  float bin_size, float cutoff, int32_t capacity);
+
+/*
+ * cpmap_slot_layout -- byte offsets of slots, over_start and over_atoms inside
+ * a slot workspace (host only, no HIP call); -1 offsets on error.
+ */
+cpmap_status cpmap_slot_layout(int64_t n_atoms,
+                               int32_t nx, int32_t ny, int32_t nz, float spacing,
+                               float ox, float oy, float oz,
+                               float bin_size, float cutoff, int32_t capacity,
+                               int64_t *slots_offset, int64_t *over_start_offset,
+                               int64_t *over_atoms_offset);
+
+/*
+ * cpmap_bin_slots -- fill a slot workspace from a binned workspace.
+ *
+ *   workspace, workspace_bytes   filled by cpmap_bin_atoms for the same n_atoms
+ *                                and geometry (else CPMAP_EGEOM); read only
+ *   n_atoms, nx..cutoff          the values given to cpmap_bin_atoms
+ *   capacity                     slots per bin, 1 .. CPMAP_MAX_SLOTS
+ *   slot_workspace               device, >= cpmap_slot_workspace_bytes(...)
+ *                                bytes, 256-byte aligned, not overlapping
+ *                                workspace (else CPMAP_EINVAL); overwritten
+ *   slot_workspace_bytes         its size (else CPMAP_ENOSPC)
+ * Records, on the host, the geometry and capacity the slot workspace was
+ * filled for, so that cpmap_cutoff_slots can check them.  Five stream-ordered
+ * launches; the result is the same on every run.  Ownership: caller owns
+ * both workspaces; they must stay valid until the work on them completes.
+ */
+cpmap_status cpmap_bin_slots(const void *workspace, size_t workspace_bytes, int64_t n_atoms,
+                             int32_t nx, int32_t ny, int32_t nz, float spacing,
+                             float ox, float oy, float oz,
+                             float bin_size, float cutoff, int32_t capacity,
+                             void *slot_workspace, size_t slot_workspace_bytes, void *stream);
+
+/*
+ * cpmap_cutoff_slots -- the cutoff sum of cpmap_cutoff_term over
+ * fixed-capacity bins.
+ *
+ * Two launches of the cutoff kernel: the first walks the slots of each
+ * tile's neighbourhood (a run of bins is a run of capacity-slot blocks) and
+ * OVERWRITES V; the second walks the overflow list and ADDS into V, leaving
+ * untouched the nodes of tiles with no overflow atom in reach (the lecture
+ * computes the overflow on the CPU).  With no overflow V equals
+ * cpmap_cutoff_term's bit for bit (the same atoms in the same order at every
+ * node); with overflow it meets the same accuracy bound.
+ *
+ *   slot_workspace, bytes   filled by cpmap_bin_slots for the same n_atoms,
+ *                           geometry and capacity (else CPMAP_EGEOM)
+ *   term                    CPMAP_TERM_SMOOTHED or CPMAP_TERM_TRUNCATED
+ * Other arguments, ownership and errors as cpmap_cutoff_term.
+ */
+cpmap_status cpmap_cutoff_slots(const void *slot_workspace, size_t slot_workspace_bytes,
+                                int64_t n_atoms,
+                                int32_t nx, int32_t ny, int32_t nz, float spacing,
+                                float ox, float oy, float oz,
+                                float bin_size, float cutoff, int32_t capacity, int32_t term,
+                                float *V, void *stream);
+
+/*
  * cpmap_extrema_workspace_bytes -- workspace of cpmap_extrema for n values
  * (at most 64 KB).  Host only, no HIP call; 0 on invalid n.
  */

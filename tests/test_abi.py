@@ -106,6 +106,56 @@ def test_bin_and_cutoff_argument_checks():
     assert lib.cpmap_cutoff_term(ws, need, 100, *LAT, 1.0, 2.0, 1, FAKE, None) == EGEOM
 
 
+def test_slot_argument_checks():
+    """Fixed-capacity entry points: capacity range, int32 slot count, sizes,
+    alignment, aliasing and the binned-for-these-arguments records, all
+    refused on the host."""
+    lib = cpmap.library()
+    need = lib.cpmap_slot_workspace_bytes(100, *LAT, 1.0, 2.0, 8)
+    bneed = lib.cpmap_bin_workspace_bytes(100, *LAT, 1.0, 2.0)
+    assert need > 0 and bneed > 0
+    for cap in (0, -1, 257):
+        assert lib.cpmap_slot_workspace_bytes(100, *LAT, 1.0, 2.0, cap) == 0
+    assert lib.cpmap_slot_workspace_bytes(100, *LAT, 1.0, 2.0, 256) > need
+    assert lib.cpmap_slot_workspace_bytes(-1, *LAT, 1.0, 2.0, 8) == 0
+    assert lib.cpmap_slot_workspace_bytes(100, *LAT, 0.0, 2.0, 8) == 0
+    # 1002^3 bins: 2 slots per bin fit an int32 slot index, 3 do not
+    big = [1000, 1000, 1000, 1.0, 0.0, 0.0, 0.0]
+    assert cpmap.bin_grid(Lattice(1000, 1000, 1000, 1.0), 1.0, 1.0) == (1002, 1002, 1002)
+    assert lib.cpmap_slot_workspace_bytes(10, *big, 1.0, 1.0, 2) > 0
+    assert lib.cpmap_slot_workspace_bytes(10, *big, 1.0, 1.0, 3) == 0
+    ws, sws = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x10000 + ((bneed + 255) // 256) * 256)
+    assert lib.cpmap_bin_slots(ws, bneed, 100, *big, 1.0, 1.0, 3, sws, need, None) == ERANGE
+    assert lib.cpmap_bin_slots(ws, bneed, 100, *LAT, 1.0, 2.0, 0, sws, need, None) == EINVAL
+    assert lib.cpmap_bin_slots(None, bneed, 100, *LAT, 1.0, 2.0, 8, sws, need, None) == EINVAL
+    assert lib.cpmap_bin_slots(ws, bneed, 100, *LAT, 1.0, 2.0, 8, None, need, None) == EINVAL
+    assert lib.cpmap_bin_slots(ws, bneed, 100, *LAT, 1.0, 2.0, 8,
+                               ctypes.c_void_p(sws.value + 16), need, None) == EINVAL
+    assert lib.cpmap_bin_slots(ws, bneed - 1, 100, *LAT, 1.0, 2.0, 8, sws, need, None) == ENOSPC
+    assert lib.cpmap_bin_slots(ws, bneed, 100, *LAT, 1.0, 2.0, 8, sws, need - 1, None) == ENOSPC
+    # the slot workspace may not overlap the binned one
+    assert lib.cpmap_bin_slots(ws, bneed, 100, *LAT, 1.0, 2.0, 8,
+                               ctypes.c_void_p(0x10000 + 256), need, None) == EINVAL
+    # never binned: refused before any HIP call
+    assert lib.cpmap_bin_slots(ws, bneed, 100, *LAT, 1.0, 2.0, 8, sws, need, None) == EGEOM
+    assert lib.cpmap_cutoff_slots(sws, need, 100, *LAT, 1.0, 2.0, 8, 0, FAKE, None) == EGEOM
+    assert lib.cpmap_cutoff_slots(sws, need, 100, *LAT, 1.0, 2.0, 8, 2, FAKE, None) == EINVAL
+    assert lib.cpmap_cutoff_slots(sws, need, 100, *LAT, 1.0, 2.0, 8, 0, None, None) == EINVAL
+    assert lib.cpmap_cutoff_slots(sws, need - 1, 100, *LAT, 1.0, 2.0, 8, 0, FAKE, None) == ENOSPC
+    assert lib.cpmap_cutoff_slots(sws, need, 100, *LAT, 1.0, 2.0, 0, 0, FAKE, None) == EINVAL
+    # layout query
+    a, b, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    assert lib.cpmap_slot_layout(100, *LAT, 1.0, 2.0, 8, ctypes.byref(a), ctypes.byref(b),
+                                 None) == EINVAL
+    assert a.value == -1 and b.value == -1
+    assert lib.cpmap_slot_layout(100, *LAT, 1.0, 2.0, 8, ctypes.byref(a), ctypes.byref(b),
+                                 ctypes.byref(c)) == OK
+    nb = cpmap.bin_grid(Lattice(8, 8, 8, 0.5), 1.0, 2.0)
+    nbins = nb[0] * nb[1] * nb[2]
+    assert a.value == 0 and b.value >= 16 * 8 * nbins and c.value >= b.value + 4 * (nbins + 1)
+    assert need >= c.value + 16 * 100 and a.value % 256 == b.value % 256 == c.value % 256 == 0
+
+
 def test_layout_query_errors():
     lib = cpmap.library()
     a, b = ctypes.c_int64(), ctypes.c_int64()
