@@ -1,0 +1,148 @@
+"""Maximum-size cases on the GPU: lattices past 2^31 nodes (64-bit node
+indices in every store and in the extrema scan) and an axis at the largest
+dimension the library accepts (node coordinates exact up to 2^24).
+
+The maps are too large to bring back whole; each check samples nodes (the
+first and last, both sides of index 2^31, the nodes near the atoms, random
+ones) and compares them with the fp64 oracle evaluated at exactly those
+nodes, under the same bound as the other parity tests.  The extrema check
+plants its extremes by construction.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import direct_coulomb_potential_amd as cpmap
+from direct_coulomb_potential_amd import Lattice
+from direct_coulomb_potential_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+BIG = Lattice(2048, 1024, 1040, 0.5)  # 2,181,038,080 nodes (8.7 GB of V)
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the gpu tests need an MI355X")
+    return torch
+
+
+@pytest.fixture
+def free_after(torch):
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _linear(lat, i, j, k):
+    return (np.asarray(k, np.int64) * lat.ny + np.asarray(j, np.int64)) * lat.nx + np.asarray(i, np.int64)
+
+
+def _sample_nodes(lat, atoms_np, seed, near=4):
+    """First/last node, nodes on both sides of index 2^31, the lattice nodes
+    nearest each atom and their neighbours, and random nodes."""
+    n = lat.n_points
+    picks = [np.array([0, 1, n - 2, n - 1], np.int64)]
+    if n > 2**31 + 8:
+        picks.append(np.arange(2**31 - 4, 2**31 + 4, dtype=np.int64))
+    rng = np.random.default_rng(seed)
+    picks.append(rng.integers(0, n, size=2000, dtype=np.int64))
+    for a in atoms_np[:64]:
+        c = np.floor((a[:3] - np.asarray(lat.origin)) / lat.spacing).astype(np.int64)
+        off = np.arange(-near, near + 1)
+        ii, jj, kk = np.meshgrid(c[0] + off, c[1] + off, c[2] + off, indexing="ij")
+        ok = (ii >= 0) & (ii < lat.nx) & (jj >= 0) & (jj < lat.ny) & (kk >= 0) & (kk < lat.nz)
+        picks.append(_linear(lat, ii[ok], jj[ok], kk[ok]))
+    return np.unique(np.concatenate(picks))
+
+
+def _gather(torch, V, nodes):
+    idx = torch.from_numpy(nodes).to(V.device)
+    return V.view(-1).index_select(0, idx).cpu().numpy()
+
+
+def _parity(Vg, Vo, S, label):
+    err = np.abs(Vg.astype(np.float64) - Vo)
+    bad = ~(err <= TOL * S)
+    if bad.any():
+        i = int(np.argmax(np.where(bad, err, -1)))
+        raise AssertionError(f"{label}: {bad.sum()} nodes out of bound; sample {i}: gpu {Vg[i]!r} "
+                             f"oracle {Vo[i]!r} S {S[i]!r}")
+
+
+def test_direct_past_2_31_nodes(torch, free_after):
+    # atoms near the far corner (indices > 2^31) and near the origin
+    far = wl.random_atoms(6, (1000.0, 480.0, 500.0), (1023.0, 511.0, 519.0), seed=51)
+    near = wl.random_atoms(4, (0.3, 0.3, 0.3), (4.0, 4.0, 4.0), seed=52)
+    atoms_np = np.concatenate([far, near])
+    print(f"[large direct] dims={BIG.dims} nodes={BIG.n_points} atoms={len(atoms_np)}", flush=True)
+    atoms = torch.from_numpy(atoms_np).cuda()
+    V = cpmap.direct(atoms, BIG)
+    nodes = _sample_nodes(BIG, atoms_np, seed=53)
+    assert nodes.max() > 2**31 and nodes.max() == BIG.n_points - 1
+    Vg = _gather(torch, V, nodes)
+    del V
+    Vo, S = oracle.direct(atoms_np, BIG.dims, BIG.spacing, BIG.origin, nodes=nodes, with_scale=True)
+    _parity(Vg, Vo, S, "direct past 2^31")
+
+
+def test_cutoff_and_slots_past_2_31_nodes(torch, free_after):
+    bs, rc = 4.0, 12.0
+    # z >= 512 A is k >= 1024, i.e. node index >= 2^31; ~8 atoms per 4 A bin
+    far = wl.random_atoms(300, (1010.0, 500.0, 506.0), (1023.5, 511.5, 519.5), seed=54)
+    near = wl.random_atoms(100, (-5.0, -5.0, -5.0), (10.0, 10.0, 10.0), seed=55)
+    atoms_np = np.concatenate([far, near])
+    print(f"[large cutoff] dims={BIG.dims} atoms={len(atoms_np)} bs={bs} rc={rc}", flush=True)
+    atoms = torch.from_numpy(atoms_np).cuda()
+    ws = cpmap.bin_atoms(atoms, BIG, bs, rc)
+    nodes = _sample_nodes(BIG, atoms_np, seed=56, near=3)
+    assert nodes.max() > 2**31
+    V = cpmap.cutoff(ws, len(atoms_np), BIG, bs, rc)
+    Vg = _gather(torch, V, nodes)
+    Vo, S = oracle.cutoff(atoms_np, BIG.dims, BIG.spacing, BIG.origin, rc, nodes=nodes,
+                          with_scale=True)
+    _parity(Vg, Vo, S, "cutoff past 2^31")
+    assert np.any(Vg[nodes > 2**31] != 0.0)
+    # fixed-capacity bins on the same atoms (the far cluster overflows 4-slot bins)
+    sws = cpmap.bin_slots(ws, len(atoms_np), BIG, bs, rc, 4)
+    n_over = int(cpmap.slot_views(sws, len(atoms_np), BIG, bs, rc, 4)[1][-1].item())
+    assert n_over > 0
+    V = cpmap.cutoff_slots(sws, len(atoms_np), BIG, bs, rc, 4, out=V)
+    _parity(_gather(torch, V, nodes), Vo, S, "cutoff slots past 2^31")
+    del V, ws, sws
+
+
+def test_extrema_past_2_31_nodes(torch, free_after):
+    n = BIG.n_points
+    V = torch.zeros(n, dtype=torch.float32, device="cuda")
+    i_min, i_max = 2**31 + 5, n - 1
+    V[i_min] = -3.0
+    V[i_max] = 7.0
+    V[2**31 - 1] = 7.0   # an equal maximum at a smaller index wins
+    V[n - 10] = float("nan")
+    idx, val = cpmap.extrema(V)
+    assert idx.cpu().tolist() == [i_min, 2**31 - 1]
+    assert val.cpu().tolist() == [-3.0, 7.0]
+    del V
+
+
+def test_direct_at_the_largest_axis(torch, free_after):
+    """nx = 2^24 (the header's largest dimension): node x = fl(ox + i*h) stays
+    exact at every i, and the last node is written."""
+    lat = Lattice(1 << 24, 2, 2, 0.25, (-3.0, 0.0, 0.0))
+    atoms_np = np.array([[1.0e6, 0.1, 0.2, 1.0], [4.0e6, 0.4, 0.3, -0.5],
+                         [-1.0, 0.2, 0.1, 2.0]], dtype=np.float32)
+    print(f"[largest axis] dims={lat.dims}", flush=True)
+    atoms = torch.from_numpy(atoms_np).cuda()
+    V = cpmap.direct(atoms, lat)
+    nodes = _sample_nodes(lat, atoms_np, seed=57)
+    assert nodes.max() == lat.n_points - 1
+    Vg = _gather(torch, V, nodes)
+    Vo, S = oracle.direct(atoms_np, lat.dims, lat.spacing, lat.origin, nodes=nodes, with_scale=True)
+    _parity(Vg, Vo, S, "largest axis")
+    with pytest.raises(cpmap.CpmapError):
+        cpmap.direct(atoms, Lattice((1 << 24) + 1, 1, 1, 0.25))
+    del V
