@@ -272,6 +272,9 @@ def bench_cutoff(torch, cpmap, wl, dev, args):
     _, per_cut = time_launches(torch, run_cut, steps, args.warmup)
     _, per_trunc = time_launches(torch, run_trunc, steps, args.warmup)
     wall_e2e, _ = time_launches(torch, run_both, steps, args.warmup)
+    _, per_pair = time_launches(torch, lambda: (run_bin(), run_cut()), steps, args.warmup)
+    graph = capture_graph(torch, lambda: (run_bin(), run_cut()))
+    _, per_graph = time_launches(torch, graph.replay, steps, args.warmup)
     cut_ms = statistics.median(per_cut)
     bin_ms = statistics.median(per_bin)
     if args.no_direct_compare:
@@ -292,6 +295,8 @@ def bench_cutoff(torch, cpmap, wl, dev, args):
         "cutoff_ms_min": min(per_cut),
         "truncated_term_ms_median": statistics.median(per_trunc),
         "end_to_end_ms_with_l2_flush": wall_e2e / steps * 1e3,
+        "bin_plus_cutoff_ms_median": statistics.median(per_pair),
+        "bin_plus_cutoff_hip_graph_ms_median": statistics.median(per_graph),
         "direct_same_atoms_ms": dir_ms,
         "speedup_vs_direct": dir_ms / (cut_ms + bin_ms),
         "hbm_gbs_algorithmic": bytes_alg / (cut_ms * 1e-3) / 1e9,
@@ -299,6 +304,21 @@ def bench_cutoff(torch, cpmap, wl, dev, args):
             "cutoff_kernel_200cube_100k_rc12.md", "direct_coulomb_potential_amd/csrc/cutoff.hip"),
         "direct_equivalent_G_evals_per_s": w.pairs / ((cut_ms + bin_ms) * 1e-3) / 1e9,
     }
+
+
+def capture_graph(torch, fn):
+    """Capture fn (library launches only) into a HIP graph on a side stream."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
 
 
 def bench_slots(torch, cpmap, w, ws, V, csr_cut_ms, steps, args, cap=8):
