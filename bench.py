@@ -27,12 +27,13 @@ sys.path.insert(0, ROOT)
 
 PEAK_FP32_TFLOPS = 157.3   # MI355X fp32 vector peak (256 CU x 2.4 GHz x 256 FLOP/clk)
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+PEAK_CLOCK_GHZ = 2.4       # engine clock the peak is quoted at
 FLOP_PER_EVAL = 10
 
 
-def measured_traffic(profile: str, source: str):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, or None
-    when the kernel source has changed since the counters were taken."""
+def profile_record(profile: str, source: str):
+    """The JSON record of a committed rocprofv3 counter summary, or None when
+    the kernel source has changed since the counters were taken."""
     import hashlib
     import re
     try:
@@ -45,7 +46,27 @@ def measured_traffic(profile: str, source: str):
         return None
     if rec.get("source_sha256") != sha:
         return None
-    return rec.get("traffic_bytes_per_launch")
+    return rec
+
+
+def measured_traffic(profile: str, source: str):
+    """HBM bytes per launch from a committed counter summary (None if stale)."""
+    rec = profile_record(profile, source)
+    return rec.get("traffic_bytes_per_launch") if rec else None
+
+
+def host_cpu():
+    """CPU model and the cores this process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0))}
 
 
 def parse():
@@ -103,6 +124,7 @@ def cpu_baseline(oracle, w, target_s):
         "unit": "G evals/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
+        **host_cpu(),
         "sample": f"{n_nodes} random nodes of the 200^3 lattice x all {w.n_atoms} atoms, fp64, "
                   f"{dt:.1f} s",
     }
@@ -173,6 +195,9 @@ def main():
             "pct_fp32_valu_peak": 100.0 * FLOP_PER_EVAL * pairs / (ms_step * 1e-3) / 1e12
             / PEAK_FP32_TFLOPS,
         })
+        prof = profile_record("direct_kernel_200cube_200k.md",
+                              "direct_coulomb_potential_amd/csrc/direct.hip")
+        clock = prof.get("clock_ghz") if prof else None
         result["roofline"] = {
             "bound": "alu",
             "achieved": achieved,
@@ -187,6 +212,10 @@ def main():
             "kernel_ms_median": statistics.median(per),
             "kernel_ms_min": min(per),
             "flop_per_eval": FLOP_PER_EVAL,
+            # the peak scaled to the engine clock the counters measured
+            "clock_ghz_measured": clock,
+            "frac_at_measured_clock": (achieved / (PEAK_FP32_TFLOPS * clock / PEAK_CLOCK_GHZ)
+                                       if clock else None),
         }
         # ion placement on the map just computed: argmin / argmax over 8M nodes
         ext_ws = torch.empty(cpmap.library().cpmap_extrema_workspace_bytes(lat.n_points),
@@ -287,7 +316,11 @@ def bench_cutoff(torch, cpmap, wl, dev, args):
                                    2, 1)
         dir_ms = statistics.median(per_dir)
     bytes_alg = 16 * w.n_atoms + 4 * lat.n_points
-    return {
+    in_cut, in_cut_note = in_cutoff_pairs(w)
+    prof = profile_record("cutoff_kernel_200cube_100k_rc12.md",
+                          "direct_coulomb_potential_amd/csrc/cutoff.hip")
+    examined = prof.get("pairs_evaluated") if prof else None
+    out = {
         "workload": w.name,
         "fixed_slots": bench_slots(torch, cpmap, w, ws, V, cut_ms, steps, args),
         "bin_ms_median": bin_ms,
@@ -303,6 +336,62 @@ def bench_cutoff(torch, cpmap, wl, dev, args):
         "hbm_traffic_bytes_per_launch": measured_traffic(
             "cutoff_kernel_200cube_100k_rc12.md", "direct_coulomb_potential_amd/csrc/cutoff.hip"),
         "direct_equivalent_G_evals_per_s": w.pairs / ((cut_ms + bin_ms) * 1e-3) / 1e9,
+        "in_cutoff_pairs": in_cut,
+        "in_cutoff_pairs_note": in_cut_note,
+        "in_cutoff_G_pairs_per_s": in_cut / (cut_ms * 1e-3) / 1e9,
+        "evaluated_pairs_from_counters": examined,
+        "evaluated_G_pairs_per_s": examined / (cut_ms * 1e-3) / 1e9 if examined else None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        out["cpu_baseline"] = cutoff_cpu_baseline(oracle, w, in_cut / lat.n_points)
+    return out
+
+
+def in_cutoff_pairs(w, n_sample=20000):
+    """Atom-node pairs with r < rc, estimated from a seeded sample of nodes
+    (each sampled node's count is exact up to ties at r = rc; the total is the
+    mean times the node count)."""
+    from scipy.spatial import cKDTree
+    lat = w.lattice
+    rng = np.random.default_rng(4321)
+    nodes = rng.integers(0, lat.n_points, size=n_sample, dtype=np.int64)
+    i = nodes % lat.nx
+    j = (nodes // lat.nx) % lat.ny
+    k = nodes // (lat.nx * lat.ny)
+    o = np.asarray(lat.origin, np.float64)
+    P = np.stack([o[0] + i * lat.spacing, o[1] + j * lat.spacing, o[2] + k * lat.spacing], 1)
+    tree = cKDTree(w.atoms[:, :3].astype(np.float64))
+    counts = tree.query_ball_point(P, w.cutoff, return_length=True)
+    mean = counts.mean()
+    sem = counts.std(ddof=1) / np.sqrt(n_sample)
+    return float(mean * lat.n_points), (f"estimated from {n_sample} random nodes: "
+                                        f"{mean:.1f} +- {sem:.1f} atoms per node")
+
+
+def cutoff_cpu_baseline(oracle, w, in_cut_per_node, target_s=4.0):
+    """The oracle's brute-force cutoff sum (every atom tested at every node),
+    as it stands, on a bounded node sample of the cutoff workload."""
+    lat = w.lattice
+    rng = np.random.default_rng(5678)
+    probe = rng.integers(0, lat.n_points, size=256, dtype=np.int64)
+    oracle.cutoff(w.atoms, lat.dims, lat.spacing, lat.origin, w.cutoff, nodes=probe[:32])
+    t0 = time.perf_counter()
+    oracle.cutoff(w.atoms, lat.dims, lat.spacing, lat.origin, w.cutoff, nodes=probe)
+    per_node = max(time.perf_counter() - t0, 1e-6) / probe.size
+    n_nodes = int(min(max(target_s / per_node, 256), lat.n_points))
+    nodes = rng.integers(0, lat.n_points, size=n_nodes, dtype=np.int64)
+    t0 = time.perf_counter()
+    oracle.cutoff(w.atoms, lat.dims, lat.spacing, lat.origin, w.cutoff, nodes=nodes)
+    dt = time.perf_counter() - t0
+    return {
+        "ms_full_map_extrapolated": dt / n_nodes * lat.n_points * 1e3,
+        "G_pair_tests_per_s": n_nodes * w.n_atoms / dt / 1e9,
+        "in_cutoff_G_pairs_per_s": n_nodes * in_cut_per_node / dt / 1e9,
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        **host_cpu(),
+        "sample": f"{n_nodes} random nodes x all {w.n_atoms} atoms (brute force), fp64, {dt:.1f} s",
     }
 
 
