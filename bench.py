@@ -78,6 +78,10 @@ def parse():
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-cutoff", action="store_true")
+    p.add_argument("--all-configs", action="store_true",
+                   help="also time the direct path on every lattice/atom configuration "
+                        "(median and minimum of 10 after 3 warm-ups) and, in the CPU "
+                        "baseline, the oracle on each configuration's checked nodes")
     p.add_argument("--only", choices=["direct", "cutoff", "copy"], default=None,
                    help="time one path only (for profiler runs); 'copy' runs the plain "
                         "256 MiB copy kernel that calibrates the HBM byte counters")
@@ -239,11 +243,76 @@ def main():
     if not args.no_cutoff and args.only in (None, "cutoff"):
         result["cutoff"] = bench_cutoff(torch, cpmap, wl, dev, args)
 
+    if args.all_configs and args.only is None:
+        result["configs"] = bench_all_configs(torch, cpmap, wl, dev,
+                                              result["roofline"].get("clock_ghz_measured"))
+
     if not args.no_cpu_baseline and args.only is None:
         import oracle
         result["cpu_baseline"] = cpu_baseline(oracle, w, args.cpu_seconds)
+        if args.all_configs:
+            result["cpu_baseline"]["per_config"] = oracle_per_config(oracle, wl)
 
     print(json.dumps(result), flush=True)
+
+
+def bench_all_configs(torch, cpmap, wl, dev, clock):
+    """The direct path on workloads 1-4 and on the cutoff workload's atoms:
+    hipEvent-timed, 3 warm-ups, then the median and minimum of 10 calls."""
+    out = {}
+    for w in (wl.plane_direct(), wl.full_direct(), wl.protein_direct(), wl.large_direct(),
+              wl.cutoff_binned()):
+        lat = w.lattice
+        atoms = torch.from_numpy(w.atoms).to(dev)
+        V = torch.empty((lat.nz, lat.ny, lat.nx), dtype=torch.float32, device=dev)
+        need = cpmap.direct_workspace_bytes(w.n_atoms, lat)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        _, per = time_launches(torch, lambda: cpmap.direct(atoms, lat, out=V, workspace=ws),
+                               10, 3)
+        med = statistics.median(per)
+        tflops = FLOP_PER_EVAL * w.pairs / (med * 1e-3) / 1e12
+        out[w.name] = {
+            "path": "direct",
+            "pairs": w.pairs,
+            "ms_median": med,
+            "ms_min": min(per),
+            "G_evals_per_s": w.pairs / (med * 1e-3) / 1e9,
+            "pct_fp32_peak": 100.0 * tflops / PEAK_FP32_TFLOPS,
+            "pct_fp32_peak_at_measured_clock": (100.0 * tflops
+                                                / (PEAK_FP32_TFLOPS * clock / PEAK_CLOCK_GHZ)
+                                                if clock else None),
+            "hbm_gbs_algorithmic": (16 * w.n_atoms + 4 * lat.n_points) / (med * 1e-3) / 1e9,
+            "plan": list(cpmap.direct_plan(w.n_atoms, lat, True)),
+        }
+        del atoms, V, ws
+    return out
+
+
+def oracle_per_config(oracle, wl):
+    """The oracle, as it stands, on each workload's checked nodes: every node
+    of the two 100x100 workloads, three z-slices plus 10^4 random nodes of the
+    200^3 ones (brute-force cutoff for the cutoff workload)."""
+    out = {}
+    for w in (wl.plane_direct(), wl.full_direct(), wl.protein_direct(), wl.large_direct(),
+              wl.cutoff_binned()):
+        lat = w.lattice
+        nodes = None if lat.n_points <= 500_000 else wl.checked_nodes(lat)
+        n_nodes = lat.n_points if nodes is None else nodes.size
+        t0 = time.perf_counter()
+        if w.cutoff:
+            oracle.cutoff(w.atoms, lat.dims, lat.spacing, lat.origin, w.cutoff, nodes=nodes)
+        else:
+            oracle.direct(w.atoms, lat.dims, lat.spacing, lat.origin, nodes=nodes)
+        dt = time.perf_counter() - t0
+        out[w.name] = {
+            "nodes": n_nodes,
+            "pairs": n_nodes * w.n_atoms,
+            "s": dt,
+            "G_evals_per_s": n_nodes * w.n_atoms / dt / 1e9,
+            "kind": "brute-force cutoff" if w.cutoff else "direct",
+            "cores": oracle.num_threads(),
+        }
+    return out
 
 
 def bench_scatter(torch, cpmap, wl, dev, args):
