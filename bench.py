@@ -285,6 +285,29 @@ def bench_all_configs(torch, cpmap, wl, dev, clock):
             "plan": list(cpmap.direct_plan(w.n_atoms, lat, True)),
         }
         del atoms, V, ws
+    # the cutoff sum on the clustered atoms: dense bins, heavy 8-slot overflow
+    w = wl.protein_direct()
+    lat, bs, rc = w.lattice, 4.0, 12.0
+    atoms = torch.from_numpy(w.atoms).to(dev)
+    V = torch.empty((lat.nz, lat.ny, lat.nx), dtype=torch.float32, device=dev)
+    ws = cpmap.bin_atoms(atoms, lat, bs, rc)
+    sws = cpmap.bin_slots(ws, w.n_atoms, lat, bs, rc, 8)
+    n_over = int(cpmap.slot_views(sws, w.n_atoms, lat, bs, rc, 8)[1][-1].item())
+    _, per_bin = time_launches(torch, lambda: cpmap.bin_atoms(atoms, lat, bs, rc, workspace=ws),
+                               10, 3)
+    _, per_cut = time_launches(torch, lambda: cpmap.cutoff(ws, w.n_atoms, lat, bs, rc, out=V),
+                               10, 3)
+    _, per_slot = time_launches(
+        torch, lambda: cpmap.cutoff_slots(sws, w.n_atoms, lat, bs, rc, 8, out=V), 10, 3)
+    out["cutoff_" + w.name + "_rc12_bin4"] = {
+        "path": "cutoff (smoothed), CSR bins and 8-slot bins",
+        "bin_ms_median": statistics.median(per_bin),
+        "cutoff_ms_median": statistics.median(per_cut),
+        "cutoff_slots_ms_median": statistics.median(per_slot),
+        "slot_overflow_fraction": n_over / w.n_atoms,
+        "speedup_vs_direct": out[w.name]["ms_median"]
+        / (statistics.median(per_cut) + statistics.median(per_bin)),
+    }
     return out
 
 

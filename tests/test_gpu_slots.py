@@ -206,3 +206,28 @@ def test_cutoff_slots_is_deterministic_and_checks_records(torch):
     with pytest.raises(cpmap.CpmapError) as e:
         cpmap.bin_slots(ws, 30_000, lat, 2.0, 5.0, 4)
     assert e.value.status in (3, 4)
+
+
+@pytest.mark.parametrize("term", ["smoothed", "truncated"])
+def test_cutoff_csr_and_slots_on_clustered_atoms(torch, term):
+    """The 40k-atom clustered workload (20 Gaussian clusters, sigma 6 A) with
+    rc = 12 A and 4 A bins: dense bins make neighbourhoods of many staging
+    chunks and overflow 8-slot bins heavily; both layouts meet the bound."""
+    w = wl.protein_direct()
+    lat, bs, rc = w.lattice, 4.0, 12.0
+    atoms = torch.from_numpy(w.atoms).cuda()
+    ws = cpmap.bin_atoms(atoms, lat, bs, rc)
+    starts, _ = cpmap.workspace_views(ws, w.n_atoms, lat, bs, rc)
+    print(f"[clustered] max atoms per bin {int(torch.diff(starts).max().item())}", flush=True)
+    Vc = cpmap.cutoff(ws, w.n_atoms, lat, bs, rc, term=term).cpu().numpy().reshape(-1)
+    sws = cpmap.bin_slots(ws, w.n_atoms, lat, bs, rc, 8)
+    n_over = int(cpmap.slot_views(sws, w.n_atoms, lat, bs, rc, 8)[1][-1].item())
+    Vs = cpmap.cutoff_slots(sws, w.n_atoms, lat, bs, rc, 8, term=term).cpu().numpy().reshape(-1)
+    nodes = wl.checked_nodes(lat, n_random=5000)
+    Vo, S = _oracle(term, w.atoms, lat, rc, nodes=nodes)
+    worst_c = _parity(Vc[nodes], Vo, S, f"clustered csr {term}")
+    worst_s = _parity(Vs[nodes], Vo, S, f"clustered slots {term}")
+    print(f"clustered {term}: {n_over} of {w.n_atoms} atoms overflow; worst |err|/S csr "
+          f"{worst_c:.3e} slots {worst_s:.3e}")
+    assert n_over > w.n_atoms // 4
+
