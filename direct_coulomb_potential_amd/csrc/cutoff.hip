@@ -167,7 +167,15 @@ constexpr int kThreads = kTile * kTile * kTile / kNx;  // 128
 constexpr int kStage = 1024;                           // atoms staged per chunk (16 KB)
 constexpr int kMaxRows = 256;                          // (cy, cz) rows per list chunk
 
-enum TermMode { kSmoothClamp = 0, kSmoothSelect = 1, kTruncated = 2 };
+// kSmoothInside and kTruncInside serve atoms within the cutoff of every node
+// of the wave, which need neither the clamp nor the inclusion test.
+enum TermMode {
+    kSmoothClamp = 0,
+    kSmoothSelect = 1,
+    kTruncated = 2,
+    kSmoothInside = 3,
+    kTruncInside = 4
+};
 
 struct CutoffParams {
     float h, o[3];
@@ -209,6 +217,13 @@ __device__ __forceinline__ void add_atom(const float4 at, const float (&x)[kNx],
             const float g = fmaf(fmaf(r2, P.gc2, P.gc1), r2, P.gc0);
             const float qm = r2 < P.rc2 ? at.w : 0.0f;
             acc[c] = fmaf(qm, rs - g, acc[c]);
+        } else if constexpr (MODE == kSmoothInside) {
+            const float r2 = fmaf(dx, dx, yz2);
+            const float rs = __builtin_amdgcn_rsqf(r2);
+            const float g = fmaf(fmaf(r2, P.gc2, P.gc1), r2, P.gc0);
+            acc[c] = fmaf(at.w, rs - g, acc[c]);
+        } else if constexpr (MODE == kTruncInside) {
+            acc[c] = fmaf(at.w, __builtin_amdgcn_rsqf(fmaf(dx, dx, yz2)), acc[c]);
         } else {
             const float r2 = fmaf(dx, dx, yz2);
             const float qm = r2 < P.rc2 ? at.w : 0.0f;
@@ -241,24 +256,25 @@ __device__ inline float exact_zero_clamp(const CutoffParams &P)
     return 0.0f;
 }
 
-template <int MODE>
+// Adds the staged atoms list[0], list[STEP], ..., list[STEP * (listed - 1)].
+template <int MODE, int STEP>
 __device__ __forceinline__ void sweep(const float4 *stage, const uint16_t *list, int32_t listed,
                                       const float (&x)[kNx], float y, float z,
                                       const CutoffParams &P, float (&acc)[kNx])
 {
     int32_t i = 0;
     for (; i + 4 <= listed; i += 4) {
-        const float4 a0 = stage[list[i + 0]];
-        const float4 a1 = stage[list[i + 1]];
-        const float4 a2 = stage[list[i + 2]];
-        const float4 a3 = stage[list[i + 3]];
+        const float4 a0 = stage[list[STEP * (i + 0)]];
+        const float4 a1 = stage[list[STEP * (i + 1)]];
+        const float4 a2 = stage[list[STEP * (i + 2)]];
+        const float4 a3 = stage[list[STEP * (i + 3)]];
         add_atom<MODE>(a0, x, y, z, P, acc);
         add_atom<MODE>(a1, x, y, z, P, acc);
         add_atom<MODE>(a2, x, y, z, P, acc);
         add_atom<MODE>(a3, x, y, z, P, acc);
     }
     for (; i < listed; ++i)
-        add_atom<MODE>(stage[list[i]], x, y, z, P, acc);
+        add_atom<MODE>(stage[list[STEP * i]], x, y, z, P, acc);
 }
 
 // SLOTS = false: the atoms are a CSR (bin_start, sorted); SLOTS = true: they
@@ -311,10 +327,14 @@ __global__ __launch_bounds__(kThreads) void cutoff_kernel(CutoffParams P0,
         x[c] = node_coord(i0 + c, P.h, P.o[0]);
     const float y = node_coord(j, P.h, P.o[1]);
     const float z = node_coord(k, P.h, P.o[2]);
-    float acc[kNx];
+    // atoms inside the cutoff of the whole wave and boundary atoms are summed
+    // apart (each in staged order), so the order does not depend on chunking
+    float acc_in[kNx], acc_bd[kNx];
 #pragma unroll
-    for (int c = 0; c < kNx; ++c)
-        acc[c] = 0.0f;
+    for (int c = 0; c < kNx; ++c) {
+        acc_in[c] = 0.0f;
+        acc_bd[c] = 0.0f;
+    }
 
     // The wave's node box (nodes past the lattice edge included: they are
     // computed and dropped, so the box only needs to contain the live ones).
@@ -326,8 +346,11 @@ __global__ __launch_bounds__(kThreads) void cutoff_kernel(CutoffParams P0,
                           node_coord((int64_t)ty * kTile + kTile - 1, P.h, P.o[1]),
                           node_coord((int64_t)tz * kTile + wave * kSlab + kSlab - 1, P.h,
                                      P.o[2])};
-    // a slightly widened radius keeps the list conservative against rounding
+    // a slightly widened radius keeps the list conservative against rounding;
+    // a slightly narrowed one keeps "inside" safely inside (r^2 below the
+    // clamp value or rc^2 at every node of the wave)
     const float keep2 = P0.rc2 * 1.0001f;
+    const float inside2 = P.rc2 * 0.9999f;
     bool any_atoms = false;
 
     for (int32_t row0 = 0; row0 < T.nrows; row0 += kMaxRows) {
@@ -395,35 +418,52 @@ __global__ __launch_bounds__(kThreads) void cutoff_kernel(CutoffParams P0,
                 stage[e] = sorted[span_src[a] + (g - span_off[a])];
             }
             __syncthreads();
-            int32_t listed = 0;
+            // inside atoms fill the list from the front, boundary atoms from
+            // the back; together they are at most m <= kStage entries
+            int32_t n_in = 0, n_bd = 0;
             for (int32_t e0 = 0; e0 < m; e0 += 64) {
                 const int32_t e = e0 + lane;
-                bool near = false;
+                bool near = false, inside = false;
                 if (e < m) {
                     const float4 at = stage[e];
                     const float gx = fmaxf(fmaxf(wlo[0] - at.x, at.x - whi[0]), 0.0f);
                     const float gy = fmaxf(fmaxf(wlo[1] - at.y, at.y - whi[1]), 0.0f);
                     const float gz = fmaxf(fmaxf(wlo[2] - at.z, at.z - whi[2]), 0.0f);
                     near = fmaf(gx, gx, fmaf(gy, gy, gz * gz)) < keep2;
+                    // distance to the farthest corner of the wave's box
+                    const float fx = fmaxf(at.x - wlo[0], whi[0] - at.x);
+                    const float fy = fmaxf(at.y - wlo[1], whi[1] - at.y);
+                    const float fz = fmaxf(at.z - wlo[2], whi[2] - at.z);
+                    inside = near && fmaf(fx, fx, fmaf(fy, fy, fz * fz)) < inside2;
                 }
-                const uint64_t vote = __ballot(near);
-                if (near) {
-                    const uint64_t below = lane == 0 ? 0ull : (vote & (~0ull >> (64 - lane)));
-                    wave_list[wave][listed + __popcll(below)] = (uint16_t)e;
-                }
-                listed += __popcll(vote);
+                const uint64_t v_in = __ballot(inside);
+                const uint64_t v_bd = __ballot(near && !inside);
+                const uint64_t lower = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+                if (inside)
+                    wave_list[wave][n_in + __popcll(v_in & lower)] = (uint16_t)e;
+                else if (near)
+                    wave_list[wave][kStage - 1 - (n_bd + __popcll(v_bd & lower))] = (uint16_t)e;
+                n_in += __popcll(v_in);
+                n_bd += __popcll(v_bd);
             }
-            listed = __builtin_amdgcn_readfirstlane(listed);
+            n_in = __builtin_amdgcn_readfirstlane(n_in);
+            n_bd = __builtin_amdgcn_readfirstlane(n_bd);
             // the list is written and read by this wave only
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            if (mode == kSmoothClamp)
-                sweep<kSmoothClamp>(stage, wave_list[wave], listed, x, y, z, P, acc);
-            else if (mode == kSmoothSelect)
-                sweep<kSmoothSelect>(stage, wave_list[wave], listed, x, y, z, P, acc);
-            else
-                sweep<kTruncated>(stage, wave_list[wave], listed, x, y, z, P, acc);
+            const uint16_t *front = wave_list[wave];
+            const uint16_t *back = wave_list[wave] + (kStage - 1);
+            if (mode == kTruncated) {
+                sweep<kTruncInside, 1>(stage, front, n_in, x, y, z, P, acc_in);
+                sweep<kTruncated, -1>(stage, back, n_bd, x, y, z, P, acc_bd);
+            } else {
+                sweep<kSmoothInside, 1>(stage, front, n_in, x, y, z, P, acc_in);
+                if (mode == kSmoothClamp)
+                    sweep<kSmoothClamp, -1>(stage, back, n_bd, x, y, z, P, acc_bd);
+                else
+                    sweep<kSmoothSelect, -1>(stage, back, n_bd, x, y, z, P, acc_bd);
+            }
             __syncthreads();
         }
     }
@@ -438,13 +478,13 @@ __global__ __launch_bounds__(kThreads) void cutoff_kernel(CutoffParams P0,
 #pragma unroll
         for (int c = 0; c < kNx; ++c)
             if (i0 + c < P.n[0])
-                out[i0 + c] += acc[c];
+                out[i0 + c] += acc_in[c] + acc_bd[c];
         return;
     }
 #pragma unroll
     for (int c = 0; c < kNx; ++c)
         if (i0 + c < P.n[0])
-            out[i0 + c] = acc[c];
+            out[i0 + c] = acc_in[c] + acc_bd[c];
 }
 
 int32_t ceil_div32(int32_t a, int32_t b) { return (a + b - 1) / b; }
