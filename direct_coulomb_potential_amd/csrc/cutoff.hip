@@ -167,15 +167,11 @@ constexpr int kThreads = kTile * kTile * kTile / kNx;  // 128
 constexpr int kStage = 1024;                           // atoms staged per chunk (16 KB)
 constexpr int kMaxRows = 256;                          // (cy, cz) rows per list chunk
 
-// kSmoothInside and kTruncInside serve atoms within the cutoff of every node
-// of the wave, which need neither the clamp nor the inclusion test.
-enum TermMode {
-    kSmoothClamp = 0,
-    kSmoothSelect = 1,
-    kTruncated = 2,
-    kSmoothInside = 3,
-    kTruncInside = 4
-};
+// kRsqInside serves atoms within the cutoff of every node of the wave, which
+// need neither the clamp nor the inclusion test: it adds q/r only (the
+// smoothed term's polynomial part of these atoms is added from their
+// moments, see Moments).
+enum TermMode { kSmoothClamp = 0, kSmoothSelect = 1, kTruncated = 2, kRsqInside = 3 };
 
 struct CutoffParams {
     float h, o[3];
@@ -217,12 +213,7 @@ __device__ __forceinline__ void add_atom(const float4 at, const float (&x)[kNx],
             const float g = fmaf(fmaf(r2, P.gc2, P.gc1), r2, P.gc0);
             const float qm = r2 < P.rc2 ? at.w : 0.0f;
             acc[c] = fmaf(qm, rs - g, acc[c]);
-        } else if constexpr (MODE == kSmoothInside) {
-            const float r2 = fmaf(dx, dx, yz2);
-            const float rs = __builtin_amdgcn_rsqf(r2);
-            const float g = fmaf(fmaf(r2, P.gc2, P.gc1), r2, P.gc0);
-            acc[c] = fmaf(at.w, rs - g, acc[c]);
-        } else if constexpr (MODE == kTruncInside) {
+        } else if constexpr (MODE == kRsqInside) {
             acc[c] = fmaf(at.w, __builtin_amdgcn_rsqf(fmaf(dx, dx, yz2)), acc[c]);
         } else {
             const float r2 = fmaf(dx, dx, yz2);
@@ -254,6 +245,92 @@ __device__ inline float exact_zero_clamp(const CutoffParams &P)
             return r2;
     }
     return 0.0f;
+}
+
+// Charge-weighted moments of a set of atoms about a centre c, with a = atom -
+// c, s = |a|^2: Q = sum q, m1 = sum q a, s2 = sum q s, m2 = sum q a a^T (xx,
+// yy, zz, xy, xz, yz), m3 = sum q s a, s4 = sum q s^2.  For every node x
+// (relative to c) the smoothed term's polynomial part over the set is the
+// exact expansion of sum q (GC0 + GC1 r^2 + GC2 r^4), r^2 = |x|^2 - 2 x.a + s:
+//   sum q r^2 = Q |x|^2 - 2 x.m1 + s2,
+//   sum q r^4 = Q |x|^4 + s4 + 4 x^T m2 x + 2 |x|^2 s2 - 4 |x|^2 x.m1 - 4 x.m3.
+struct Moments {
+    float q, m1[3], s2, m2[6], m3[3], s4;
+};
+
+__device__ __forceinline__ void moments_zero(Moments &M)
+{
+    M.q = M.s2 = M.s4 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+        M.m1[i] = M.m3[i] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 6; ++i)
+        M.m2[i] = 0.0f;
+}
+
+__device__ __forceinline__ void moments_add(Moments &M, const float4 at, const float (&c)[3])
+{
+    const float ax = at.x - c[0], ay = at.y - c[1], az = at.z - c[2];
+    const float s = fmaf(ax, ax, fmaf(ay, ay, az * az));
+    const float qx = at.w * ax, qy = at.w * ay, qz = at.w * az, qs = at.w * s;
+    M.q += at.w;
+    M.m1[0] += qx;
+    M.m1[1] += qy;
+    M.m1[2] += qz;
+    M.s2 += qs;
+    M.m2[0] = fmaf(qx, ax, M.m2[0]);
+    M.m2[1] = fmaf(qy, ay, M.m2[1]);
+    M.m2[2] = fmaf(qz, az, M.m2[2]);
+    M.m2[3] = fmaf(qx, ay, M.m2[3]);
+    M.m2[4] = fmaf(qx, az, M.m2[4]);
+    M.m2[5] = fmaf(qy, az, M.m2[5]);
+    M.m3[0] = fmaf(qs, ax, M.m3[0]);
+    M.m3[1] = fmaf(qs, ay, M.m3[1]);
+    M.m3[2] = fmaf(qs, az, M.m3[2]);
+    M.s4 = fmaf(qs, s, M.s4);
+}
+
+// Sum over the wave's 64 lanes by an xor butterfly: both partners of a step
+// add the same two values, so every lane ends with the same total.
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1)
+        v += __shfl_xor(v, m);
+    return v;
+}
+
+__device__ __forceinline__ void moments_reduce(Moments &M)
+{
+    M.q = wave_sum(M.q);
+    M.s2 = wave_sum(M.s2);
+    M.s4 = wave_sum(M.s4);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        M.m1[i] = wave_sum(M.m1[i]);
+        M.m3[i] = wave_sum(M.m3[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 6; ++i)
+        M.m2[i] = wave_sum(M.m2[i]);
+}
+
+// sum q (GC0 + GC1 r^2 + GC2 r^4) over the moments' atoms at node x (relative
+// to their centre).
+__device__ __forceinline__ float moments_poly(const Moments &M, float x, float y, float z,
+                                              const CutoffParams &P)
+{
+    const float xx = fmaf(x, x, fmaf(y, y, z * z));
+    const float xm1 = fmaf(x, M.m1[0], fmaf(y, M.m1[1], z * M.m1[2]));
+    const float xm3 = fmaf(x, M.m3[0], fmaf(y, M.m3[1], z * M.m3[2]));
+    const float diag = fmaf(M.m2[0] * x, x, fmaf(M.m2[1] * y, y, M.m2[2] * z * z));
+    const float off = fmaf(M.m2[3] * x, y, fmaf(M.m2[4] * x, z, M.m2[5] * y * z));
+    const float xm2x = fmaf(2.0f, off, diag);
+    const float p2 = fmaf(M.q, xx, fmaf(-2.0f, xm1, M.s2));
+    const float p4 = fmaf(M.q * xx, xx, M.s4) + 4.0f * xm2x + 2.0f * xx * M.s2 -
+                     4.0f * xx * xm1 - 4.0f * xm3;
+    return fmaf(P.gc2, p4, fmaf(P.gc1, p2, P.gc0 * M.q));
 }
 
 // Adds the staged atoms list[0], list[STEP], ..., list[STEP * (listed - 1)].
@@ -335,6 +412,12 @@ __global__ __launch_bounds__(kThreads) void cutoff_kernel(CutoffParams P0,
         acc_in[c] = 0.0f;
         acc_bd[c] = 0.0f;
     }
+    // the smoothed term's polynomial part over the inside atoms, from their
+    // moments about the wave's centre: lane l accumulates the tile's inside
+    // atoms number l, l + 64, ... (counted in staged order over all chunks)
+    Moments mom;
+    moments_zero(mom);
+    int32_t inside_seen = 0;
 
     // The wave's node box (nodes past the lattice edge included: they are
     // computed and dropped, so the box only needs to contain the live ones).
@@ -351,6 +434,8 @@ __global__ __launch_bounds__(kThreads) void cutoff_kernel(CutoffParams P0,
     // clamp value or rc^2 at every node of the wave)
     const float keep2 = P0.rc2 * 1.0001f;
     const float inside2 = P.rc2 * 0.9999f;
+    const float centre[3] = {0.5f * (wlo[0] + whi[0]), 0.5f * (wlo[1] + whi[1]),
+                             0.5f * (wlo[2] + whi[2])};
     bool any_atoms = false;
 
     for (int32_t row0 = 0; row0 < T.nrows; row0 += kMaxRows) {
@@ -454,11 +539,13 @@ __global__ __launch_bounds__(kThreads) void cutoff_kernel(CutoffParams P0,
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             const uint16_t *front = wave_list[wave];
             const uint16_t *back = wave_list[wave] + (kStage - 1);
+            sweep<kRsqInside, 1>(stage, front, n_in, x, y, z, P, acc_in);
             if (mode == kTruncated) {
-                sweep<kTruncInside, 1>(stage, front, n_in, x, y, z, P, acc_in);
                 sweep<kTruncated, -1>(stage, back, n_bd, x, y, z, P, acc_bd);
             } else {
-                sweep<kSmoothInside, 1>(stage, front, n_in, x, y, z, P, acc_in);
+                for (int32_t i = (lane - inside_seen) & 63; i < n_in; i += 64)
+                    moments_add(mom, stage[front[i]], centre);
+                inside_seen += n_in;
                 if (mode == kSmoothClamp)
                     sweep<kSmoothClamp, -1>(stage, back, n_bd, x, y, z, P, acc_bd);
                 else
@@ -466,6 +553,14 @@ __global__ __launch_bounds__(kThreads) void cutoff_kernel(CutoffParams P0,
             }
             __syncthreads();
         }
+    }
+
+    if (mode != kTruncated) {
+        // every lane of the wave takes part in the reduction
+        moments_reduce(mom);
+#pragma unroll
+        for (int c = 0; c < kNx; ++c)
+            acc_in[c] -= moments_poly(mom, x[c] - centre[0], y - centre[1], z - centre[2], P);
     }
 
     if (j >= P.n[1] || k >= P.n[2])
