@@ -20,12 +20,16 @@
 //    and needs no table;
 //  - the spans' atoms are staged into LDS (the lecture's "fetch bins of data
 //    into shared memory", one bin at a time there; all spans at once here, in
-//    chunks of kStage atoms when the neighbourhood is larger);
-//  - each wave owns an 8x8x4 slab of the tile and keeps, in an LDS index list,
-//    only the staged atoms within rc of its slab's node box (one atom per
-//    lane tested, ballot + prefix count), which removes about 40% of the
-//    examined pairs at 4 A bins; this is the lecture's "sphere of bins" idea
-//    applied per wave at atom granularity;
+//    chunks of kStage atoms, small enough that LDS allows 5 resident waves
+//    per SIMD);
+//  - each wave owns an 8x8x4 slab of the tile and keeps, in an LDS list of
+//    byte offsets into the stage, only the staged atoms within rc of its
+//    slab's node box (one atom per lane tested, ballot + prefix count), which
+//    removes about 40% of the examined pairs at 4 A bins; this is the
+//    lecture's "sphere of bins" idea applied per wave at atom granularity;
+//    atoms within rc of the whole box go to the front of the list and skip
+//    the cutoff test, the smoothed term's polynomial part of those atoms
+//    coming from their moments (see Moments);
 //  - each lane owns kNx consecutive nodes of one x-row, reads its wave's
 //    listed atoms as LDS broadcasts, shares dy and dz across its nodes, and
 //    adds the term with r^2 clamped to the largest value <= rc^2 at which the
@@ -124,10 +128,13 @@ __host__ __device__ inline bool row_run(double xlo, double xhi, double b0x, doub
     return true;
 }
 
+// A tile's node box, its candidate bin rows, and the bin geometry the rows
+// are tested against (in double, as the neighbourhood is decided).
 struct TileRows {
     double lo[3], hi[3];
+    double b0[3], bs, rc;
     AxisRange ry, rz;
-    int32_t ncy, nrows;
+    int32_t nbx, ncy, nrows;
 };
 
 __host__ __device__ inline TileRows tile_rows(int32_t tx, int32_t ty, int32_t tz,
@@ -136,6 +143,11 @@ __host__ __device__ inline TileRows tile_rows(int32_t tx, int32_t ty, int32_t tz
                                               float rc)
 {
     TileRows T;
+    for (int a = 0; a < 3; ++a)
+        T.b0[a] = (double)b0[a];
+    T.bs = (double)bs;
+    T.rc = (double)rc;
+    T.nbx = nb[0];
     tile_box(tx, n[0], h, o[0], &T.lo[0], &T.hi[0]);
     tile_box(ty, n[1], h, o[1], &T.lo[1], &T.hi[1]);
     tile_box(tz, n[2], h, o[2], &T.lo[2], &T.hi[2]);
@@ -148,24 +160,28 @@ __host__ __device__ inline TileRows tile_rows(int32_t tx, int32_t ty, int32_t tz
 }
 
 // Row rr of a tile's candidate rows (z-major, then y) -> its bins' x-run.
-__host__ __device__ inline bool tile_row(const TileRows &T, int32_t rr, const float b0[3],
-                                         const int32_t nb[3], float bs, float rc, int32_t *cy,
+__host__ __device__ inline bool tile_row(const TileRows &T, int32_t rr, int32_t *cy,
                                          int32_t *cz, int32_t *cx0, int32_t *cx1)
 {
     *cy = T.ry.first + rr % T.ncy;
     *cz = T.rz.first + rr / T.ncy;
-    const double gy = axis_gap(T.lo[1], T.hi[1], (double)b0[1], (double)bs, *cy);
-    const double gz = axis_gap(T.lo[2], T.hi[2], (double)b0[2], (double)bs, *cz);
-    return row_run(T.lo[0], T.hi[0], (double)b0[0], (double)bs, nb[0], (double)rc,
-                   gy * gy + gz * gz, cx0, cx1);
+    const double gy = axis_gap(T.lo[1], T.hi[1], T.b0[1], T.bs, *cy);
+    const double gz = axis_gap(T.lo[2], T.hi[2], T.b0[2], T.bs, *cz);
+    return row_run(T.lo[0], T.hi[0], T.b0[0], T.bs, T.nbx, T.rc, gy * gy + gz * gz, cx0, cx1);
 }
 
 // ---- kernel -------------------------------------------------------------------
 
 constexpr int kNx = 4;                                 // nodes per lane along x
 constexpr int kThreads = kTile * kTile * kTile / kNx;  // 128
-constexpr int kStage = 1024;                           // atoms staged per chunk (16 KB)
+constexpr int kStage = 512;                            // atoms staged per chunk (8 KB)
 constexpr int kMaxRows = 256;                          // (cy, cz) rows per list chunk
+// Resident waves per SIMD the kernel is built for: the sweep is latency-bound
+// on its LDS reads below this (measured 1.74 ms at 4 waves, 1.66 ms at 5 on
+// the 100k-atom rc = 12 A map); at 5 the register budget is 102 VGPRs and the
+// few spills the compiler adds sit outside the sweep loops.  LDS per
+// workgroup (about 15 KB) allows 5 as well.
+constexpr int kWavesPerSimd = 5;
 
 // kRsqInside serves atoms within the cutoff of every node of the wave, which
 // need neither the clamp nor the inclusion test: it adds q/r only (the
@@ -333,41 +349,47 @@ __device__ __forceinline__ float moments_poly(const Moments &M, float x, float y
     return fmaf(P.gc2, p4, fmaf(P.gc1, p2, P.gc0 * M.q));
 }
 
-// Adds the staged atoms list[0], list[STEP], ..., list[STEP * (listed - 1)].
+// The staged atom at byte offset off of the stage array.
+__device__ __forceinline__ float4 staged(const float4 *stage, uint32_t off)
+{
+    return *reinterpret_cast<const float4 *>(reinterpret_cast<const char *>(stage) + off);
+}
+
+// Adds the staged atoms at byte offsets list[0], list[STEP], ...,
+// list[STEP * (listed - 1)].
 template <int MODE, int STEP>
-__device__ __forceinline__ void sweep(const float4 *stage, const uint16_t *list, int32_t listed,
+__device__ __forceinline__ void sweep(const float4 *stage, const uint32_t *list, int32_t listed,
                                       const float (&x)[kNx], float y, float z,
                                       const CutoffParams &P, float (&acc)[kNx])
 {
     int32_t i = 0;
     for (; i + 4 <= listed; i += 4) {
-        const float4 a0 = stage[list[STEP * (i + 0)]];
-        const float4 a1 = stage[list[STEP * (i + 1)]];
-        const float4 a2 = stage[list[STEP * (i + 2)]];
-        const float4 a3 = stage[list[STEP * (i + 3)]];
+        const float4 a0 = staged(stage, list[STEP * (i + 0)]);
+        const float4 a1 = staged(stage, list[STEP * (i + 1)]);
+        const float4 a2 = staged(stage, list[STEP * (i + 2)]);
+        const float4 a3 = staged(stage, list[STEP * (i + 3)]);
         add_atom<MODE>(a0, x, y, z, P, acc);
         add_atom<MODE>(a1, x, y, z, P, acc);
         add_atom<MODE>(a2, x, y, z, P, acc);
         add_atom<MODE>(a3, x, y, z, P, acc);
     }
     for (; i < listed; ++i)
-        add_atom<MODE>(stage[list[STEP * i]], x, y, z, P, acc);
+        add_atom<MODE>(staged(stage, list[STEP * i]), x, y, z, P, acc);
 }
 
 // SLOTS = false: the atoms are a CSR (bin_start, sorted); SLOTS = true: they
 // are fixed-capacity bins, bin b's slots at sorted[b * cap ...], and
 // bin_start is not read.  ACCUM = true adds the sum into V.
 template <bool SLOTS, bool ACCUM>
-__global__ __launch_bounds__(kThreads) void cutoff_kernel(CutoffParams P0,
-                                                          const int32_t *__restrict__ bin_start,
-                                                          const float4 *__restrict__ sorted,
-                                                          int32_t n_sorted, float *__restrict__ V)
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd))) void
+cutoff_kernel(CutoffParams P0, const int32_t *__restrict__ bin_start,
+              const float4 *__restrict__ sorted, int32_t n_sorted, float *__restrict__ V)
 {
     __shared__ float4 stage[kStage];
-    __shared__ uint16_t wave_list[kWaves][kStage];
+    __shared__ uint32_t wave_list[kWaves][kStage];  // byte offsets into stage
     __shared__ int32_t span_src[kMaxRows];
     __shared__ int32_t span_off[kMaxRows + 1];
-    __shared__ int32_t scan_tmp[kThreads];
+    __shared__ int32_t wave_total[kWaves];
 
     // Smoothed term: clamp r^2 where a clamp value with an exactly-zero term
     // exists, else select.  Truncated term: select.
@@ -388,7 +410,12 @@ __global__ __launch_bounds__(kThreads) void cutoff_kernel(CutoffParams P0,
     const int32_t tx = tile % P.tiles[0];
     const int32_t ty = (tile / P.tiles[0]) % P.tiles[1];
     const int32_t tz = tile / (P.tiles[0] * P.tiles[1]);
-    const TileRows T = tile_rows(tx, ty, tz, P.n, P.h, P.o, P.b0, P.nb, P.bs, P.list_rc);
+    // The tile's geometry is the same for every thread: computed once and
+    // kept in LDS, so its doubles do not occupy registers through the sweep.
+    __shared__ TileRows T;
+    if (t == 0)
+        T = tile_rows(tx, ty, tz, P.n, P.h, P.o, P.b0, P.nb, P.bs, P.list_rc);
+    __syncthreads();
 
     // This lane's nodes: an x-run of kNx nodes in one row of one plane; the
     // wave's 64 lanes cover 8 x 8 x (kTile / kWaves) nodes.
@@ -447,7 +474,7 @@ __global__ __launch_bounds__(kThreads) void cutoff_kernel(CutoffParams P0,
         int32_t local = 0;
         for (int32_t r = r_lo; r < r_hi; ++r) {
             int32_t cy, cz, cx0, cx1, cnt = 0, src = 0;
-            if (tile_row(T, row0 + r, P.b0, P.nb, P.bs, P.list_rc, &cy, &cz, &cx0, &cx1)) {
+            if (tile_row(T, row0 + r, &cy, &cz, &cx0, &cx1)) {
                 const int64_t base = ((int64_t)cz * P.nb[1] + cy) * P.nb[0];
                 if constexpr (SLOTS) {
                     src = (int32_t)((base + cx0) * P.cap);
@@ -465,22 +492,36 @@ __global__ __launch_bounds__(kThreads) void cutoff_kernel(CutoffParams P0,
             span_off[r] = cnt;
             local += cnt;
         }
-        // 2. exclusive offsets of the spans in row order
-        scan_tmp[t] = local;
-        __syncthreads();
-        for (int off = 1; off < kThreads; off <<= 1) {
-            const int32_t v = t >= off ? scan_tmp[t - off] : 0;
-            __syncthreads();
-            scan_tmp[t] += v;
-            __syncthreads();
+        // 2. exclusive offsets of the spans in row order: a scan inside each
+        //    wave, then the waves' totals through LDS
+        // (the lane id goes through an empty asm so that the shuffle
+        // addresses are formed here, not kept in registers through the sweep)
+        int32_t lid = lane;
+        asm volatile("" : "+v"(lid));
+        int32_t incl = local;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int32_t v = __builtin_amdgcn_ds_bpermute((lid - off) << 2, incl);
+            if (lid >= off)
+                incl += v;
         }
-        int32_t run = scan_tmp[t] - local;
+        if (lane == 63)
+            wave_total[wave] = incl;
+        __syncthreads();
+        int32_t run = incl - local;
+        int32_t sum = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const int32_t wt = wave_total[w];
+            run += w < wave ? wt : 0;
+            sum += wt;
+        }
         for (int32_t r = r_lo; r < r_hi; ++r) {
             const int32_t c = span_off[r];
             span_off[r] = run;
             run += c;
         }
-        const int32_t total = __builtin_amdgcn_readfirstlane(scan_tmp[kThreads - 1]);
+        const int32_t total = __builtin_amdgcn_readfirstlane(sum);
         if (t == 0)
             span_off[rows] = total;
         any_atoms |= total > 0;
@@ -525,9 +566,10 @@ __global__ __launch_bounds__(kThreads) void cutoff_kernel(CutoffParams P0,
                 const uint64_t v_bd = __ballot(near && !inside);
                 const uint64_t lower = lane == 0 ? 0ull : (~0ull >> (64 - lane));
                 if (inside)
-                    wave_list[wave][n_in + __popcll(v_in & lower)] = (uint16_t)e;
+                    wave_list[wave][n_in + __popcll(v_in & lower)] = (uint32_t)e * 16u;
                 else if (near)
-                    wave_list[wave][kStage - 1 - (n_bd + __popcll(v_bd & lower))] = (uint16_t)e;
+                    wave_list[wave][kStage - 1 - (n_bd + __popcll(v_bd & lower))] =
+                        (uint32_t)e * 16u;
                 n_in += __popcll(v_in);
                 n_bd += __popcll(v_bd);
             }
@@ -537,14 +579,14 @@ __global__ __launch_bounds__(kThreads) void cutoff_kernel(CutoffParams P0,
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            const uint16_t *front = wave_list[wave];
-            const uint16_t *back = wave_list[wave] + (kStage - 1);
+            const uint32_t *front = wave_list[wave];
+            const uint32_t *back = wave_list[wave] + (kStage - 1);
             sweep<kRsqInside, 1>(stage, front, n_in, x, y, z, P, acc_in);
             if (mode == kTruncated) {
                 sweep<kTruncated, -1>(stage, back, n_bd, x, y, z, P, acc_bd);
             } else {
                 for (int32_t i = (lane - inside_seen) & 63; i < n_in; i += 64)
-                    moments_add(mom, stage[front[i]], centre);
+                    moments_add(mom, staged(stage, front[i]), centre);
                 inside_seen += n_in;
                 if (mode == kSmoothClamp)
                     sweep<kSmoothClamp, -1>(stage, back, n_bd, x, y, z, P, acc_bd);
@@ -563,23 +605,30 @@ __global__ __launch_bounds__(kThreads) void cutoff_kernel(CutoffParams P0,
             acc_in[c] -= moments_poly(mom, x[c] - centre[0], y - centre[1], z - centre[2], P);
     }
 
-    if (j >= P.n[1] || k >= P.n[2])
+    // The store's indices again: cheaper to recompute than to keep through
+    // the sweep (the empty asm keeps the compiler from reusing the early ones).
+    int32_t te = threadIdx.x;
+    asm volatile("" : "+v"(te));
+    const int32_t i0s = tx * kTile + (te % (kTile / kNx)) * kNx;
+    const int32_t js = ty * kTile + (te / (kTile / kNx)) % kTile;
+    const int32_t ks = tz * kTile + te / (kTile / kNx * kTile);
+    if (js >= P.n[1] || ks >= P.n[2])
         return;
-    float *out = V + ((int64_t)k * P.n[1] + j) * P.n[0];
+    float *out = V + ((int64_t)ks * P.n[1] + js) * P.n[0];
     if constexpr (ACCUM) {
         // nothing within reach of this tile: its nodes keep their value
         if (!any_atoms)
             return;
 #pragma unroll
         for (int c = 0; c < kNx; ++c)
-            if (i0 + c < P.n[0])
-                out[i0 + c] += acc_in[c] + acc_bd[c];
+            if (i0s + c < P.n[0])
+                out[i0s + c] += acc_in[c] + acc_bd[c];
         return;
     }
 #pragma unroll
     for (int c = 0; c < kNx; ++c)
-        if (i0 + c < P.n[0])
-            out[i0 + c] = acc_in[c] + acc_bd[c];
+        if (i0s + c < P.n[0])
+            out[i0s + c] = acc_in[c] + acc_bd[c];
 }
 
 int32_t ceil_div32(int32_t a, int32_t b) { return (a + b - 1) / b; }
@@ -686,7 +735,7 @@ extern "C" int64_t cpmap_neighbor_spans(int32_t nx, int32_t ny, int32_t nz, floa
     int64_t count = 0;
     for (int32_t r = 0; r < T.nrows; ++r) {
         int32_t cy, cz, cx0, cx1;
-        if (!tile_row(T, r, b0, nb, bin_size, cutoff, &cy, &cz, &cx0, &cx1))
+        if (!tile_row(T, r, &cy, &cz, &cx0, &cx1))
             continue;
         if (count < max_spans) {
             spans_out[4 * count + 0] = cy;
