@@ -9,7 +9,8 @@
 // geometry.  The sort is a stable LSD radix sort on the bin id (8-bit digits,
 // as many passes as the bin count needs), so atoms keep their input order
 // inside a bin and the output is bit-identical from run to run:
-//   keys      bin id per atom (nbins for dropped atoms, which sort last)
+//   keys      bin id per atom (nbins for dropped atoms, which sort last),
+//             formed by the first pass's histogram kernel
 //   per pass  tile histograms -> one exclusive scan (digit-major) -> stable
 //             scatter, ranking equal digits inside a wave with ballots
 //   starts    bin_start[b] = lower_bound(sorted keys, b)
@@ -26,31 +27,32 @@ constexpr int kDigits = 256;
 
 size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
 
-__global__ void k_keys(const float4 *__restrict__ atoms, int32_t n, float b0x, float b0y,
-                       float b0z, int32_t nbx, int32_t nby, int32_t nbz, float bs,
-                       int32_t nbins, int32_t *__restrict__ keys, int32_t *__restrict__ vals)
+struct KeyGeometry {
+    float b0x, b0y, b0z, bs;
+    int32_t nbx, nby, nbz, nbins;
+};
+
+// Bin id of an atom, or nbins when it lies outside the bin grid.
+__device__ __forceinline__ int32_t atom_key(const float4 a, const KeyGeometry &G)
 {
-    const int32_t i = blockIdx.x * kThreads + threadIdx.x;
-    if (i >= n)
-        return;
-    const float4 a = atoms[i];
-    const float tx = bin_coord(a.x, b0x, bs);
-    const float ty = bin_coord(a.y, b0y, bs);
-    const float tz = bin_coord(a.z, b0z, bs);
-    const bool keep = tx >= 0.0f && tx < (float)nbx && ty >= 0.0f && ty < (float)nby &&
-                      tz >= 0.0f && tz < (float)nbz;
-    int32_t key = nbins;
-    if (keep) {
-        const int32_t cx = (int32_t)floorf(tx), cy = (int32_t)floorf(ty),
-                      cz = (int32_t)floorf(tz);
-        key = (cz * nby + cy) * nbx + cx;
-    }
-    keys[i] = key;
-    vals[i] = i;
+    const float tx = bin_coord(a.x, G.b0x, G.bs);
+    const float ty = bin_coord(a.y, G.b0y, G.bs);
+    const float tz = bin_coord(a.z, G.b0z, G.bs);
+    const bool keep = tx >= 0.0f && tx < (float)G.nbx && ty >= 0.0f && ty < (float)G.nby &&
+                      tz >= 0.0f && tz < (float)G.nbz;
+    if (!keep)
+        return G.nbins;
+    const int32_t cx = (int32_t)floorf(tx), cy = (int32_t)floorf(ty), cz = (int32_t)floorf(tz);
+    return (cz * G.nby + cy) * G.nbx + cx;
 }
 
 // Digit counts of one tile, written digit-major: hist[d * n_tiles + tile].
-__global__ __launch_bounds__(kThreads) void k_hist(const int32_t *__restrict__ keys, int32_t n,
+// FIRST: the first pass, which also forms the keys from the atoms and writes
+// them with their input positions.
+template <bool FIRST>
+__global__ __launch_bounds__(kThreads) void k_hist(const float4 *__restrict__ atoms,
+                                                   KeyGeometry G, int32_t *__restrict__ keys,
+                                                   int32_t *__restrict__ vals, int32_t n,
                                                    int shift, int32_t n_tiles,
                                                    int32_t *__restrict__ hist)
 {
@@ -61,38 +63,71 @@ __global__ __launch_bounds__(kThreads) void k_hist(const int32_t *__restrict__ k
 #pragma unroll
     for (int it = 0; it < kItems; ++it) {
         const int64_t e = base + it * kThreads + threadIdx.x;
-        if (e < n)
-            atomicAdd(&cnt[(keys[e] >> shift) & 0xff], 1);
+        if (e < n) {
+            int32_t key;
+            if constexpr (FIRST) {
+                key = atom_key(atoms[e], G);
+                keys[e] = key;
+                vals[e] = (int32_t)e;
+            } else {
+                key = keys[e];
+            }
+            atomicAdd(&cnt[(key >> shift) & 0xff], 1);
+        }
     }
     __syncthreads();
     hist[(int64_t)threadIdx.x * n_tiles + blockIdx.x] = cnt[threadIdx.x];
 }
 
-// Exclusive scan of m int32 in place, one workgroup of 1024 threads: each
-// thread scans a contiguous segment, the segment sums are scanned in LDS.
-__global__ __launch_bounds__(1024) void k_scan(int32_t *__restrict__ data, int64_t m)
+// Exclusive scan of m int32 in place by one workgroup of 1024 threads, in
+// rounds of 1024 x kScanPer values: each thread loads its kScanPer
+// consecutive values at once, the threads' sums are scanned inside each wave
+// with shuffles and across the 16 waves through LDS, and a carry links the
+// rounds.
+constexpr int kScanThreads = 1024;
+constexpr int kScanPer = 16;
+
+__global__ __launch_bounds__(kScanThreads) void k_scan(int32_t *__restrict__ data, int64_t m)
 {
-    __shared__ int32_t part[1024];
+    __shared__ int32_t wave_sum[kScanThreads / 64];
     const int t = threadIdx.x;
-    const int64_t seg = (m + 1023) / 1024;
-    const int64_t lo = t * seg < m ? t * seg : m;
-    const int64_t hi = lo + seg < m ? lo + seg : m;
-    int32_t s = 0;
-    for (int64_t i = lo; i < hi; ++i)
-        s += data[i];
-    part[t] = s;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-        const int32_t v = t >= off ? part[t - off] : 0;
+    const int lane = t % 64;
+    const int wave = t / 64;
+    int32_t carry = 0;
+    for (int64_t base = 0; base < m; base += (int64_t)kScanThreads * kScanPer) {
+        const int64_t lo = base + (int64_t)t * kScanPer;
+        int32_t v[kScanPer];
+        int32_t s = 0;
+#pragma unroll
+        for (int k = 0; k < kScanPer; ++k) {
+            v[k] = lo + k < m ? data[lo + k] : 0;
+            s += v[k];
+        }
+        int32_t incl = s;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int32_t u = __shfl_up(incl, off);
+            if (lane >= off)
+                incl += u;
+        }
+        if (lane == 63)
+            wave_sum[wave] = incl;
         __syncthreads();
-        part[t] += v;
-        __syncthreads();
-    }
-    int32_t run = part[t] - s;  // exclusive prefix of this segment
-    for (int64_t i = lo; i < hi; ++i) {
-        const int32_t v = data[i];
-        data[i] = run;
-        run += v;
+        int32_t run = carry + incl - s;
+        int32_t total = 0;
+        for (int w = 0; w < kScanThreads / 64; ++w) {
+            const int32_t ws = wave_sum[w];
+            run += w < wave ? ws : 0;
+            total += ws;
+        }
+#pragma unroll
+        for (int k = 0; k < kScanPer; ++k) {
+            if (lo + k < m)
+                data[lo + k] = run;
+            run += v[k];
+        }
+        carry += total;
+        __syncthreads();  // wave_sum is rewritten by the next round
     }
 }
 
@@ -229,16 +264,26 @@ hipError_t launch_bin_atoms(const float4 *atoms, int64_t n_atoms, const Lattice 
     int32_t *hist = reinterpret_cast<int32_t *>(ws + L.hist);
 
     if (n > 0) {
-        hipLaunchKernelGGL(k_keys, dim3(grid_for(n)), dim3(kThreads), 0, stream, atoms, n,
-                           g.ax[0].b0, g.ax[1].b0, g.ax[2].b0, g.ax[0].nb, g.ax[1].nb, g.ax[2].nb,
-                           g.bin_size, nbins, keys[0], vals[0]);
+        KeyGeometry G;
+        G.b0x = g.ax[0].b0;
+        G.b0y = g.ax[1].b0;
+        G.b0z = g.ax[2].b0;
+        G.bs = g.bin_size;
+        G.nbx = g.ax[0].nb;
+        G.nby = g.ax[1].nb;
+        G.nbz = g.ax[2].nb;
+        G.nbins = nbins;
         const int32_t tiles = (int32_t)L.n_tiles;
         for (int p = 0; p < L.passes; ++p) {
             const int shift = 8 * p;
             const int src = p & 1, dst = src ^ 1;
-            hipLaunchKernelGGL(k_hist, dim3(tiles), dim3(kThreads), 0, stream, keys[src], n,
-                               shift, tiles, hist);
-            hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, stream, hist,
+            if (p == 0)
+                hipLaunchKernelGGL(k_hist<true>, dim3(tiles), dim3(kThreads), 0, stream, atoms,
+                                   G, keys[0], vals[0], n, shift, tiles, hist);
+            else
+                hipLaunchKernelGGL(k_hist<false>, dim3(tiles), dim3(kThreads), 0, stream, atoms,
+                                   G, keys[src], vals[src], n, shift, tiles, hist);
+            hipLaunchKernelGGL(k_scan, dim3(1), dim3(kScanThreads), 0, stream, hist,
                                (int64_t)kDigits * tiles);
             hipLaunchKernelGGL(k_scatter, dim3(tiles), dim3(kThreads), 0, stream, keys[src],
                                vals[src], n, shift, tiles, hist, keys[dst], vals[dst]);
