@@ -131,7 +131,10 @@ cpmap_status make_bin_geometry(int32_t nx, int32_t ny, int32_t nz, float h, floa
         if (st != CPMAP_OK)
             return st;
     }
-    if (g->nbins() >= (int64_t)INT32_MAX)
+    // each axis has at most 2^24 bins, so bound the first two axes' product
+    // (< 2^48) before multiplying by the third
+    const int64_t plane = (int64_t)g->ax[0].nb * g->ax[1].nb;
+    if (plane >= (int64_t)INT32_MAX || plane * g->ax[2].nb >= (int64_t)INT32_MAX)
         return CPMAP_ERANGE;
     return CPMAP_OK;
 }
