@@ -156,6 +156,17 @@ def test_slot_argument_checks():
     assert need >= c.value + 16 * 100 and a.value % 256 == b.value % 256 == c.value % 256 == 0
 
 
+def test_bin_count_overflow_is_range_error():
+    """Per-axis bin counts near 2^24 multiply past int64: the geometry check
+    bounds the product step by step and reports ERANGE."""
+    lib = cpmap.library()
+    dims = (ctypes.c_int32 * 3)()
+    # a 2x2x2 lattice 160 A apart in 1e-5 A bins: ~1.6e7 bins per axis
+    assert lib.cpmap_bin_grid(2, 2, 2, 160.0, 0.0, 0.0, 0.0, 1e-5, 1e-5, dims) == ERANGE
+    assert lib.cpmap_bin_workspace_bytes(10, 2, 2, 2, 160.0, 0.0, 0.0, 0.0, 1e-5, 1e-5) == 0
+    assert lib.cpmap_slot_workspace_bytes(10, 2, 2, 2, 160.0, 0.0, 0.0, 0.0, 1e-5, 1e-5, 8) == 0
+
+
 def test_layout_query_errors():
     lib = cpmap.library()
     a, b = ctypes.c_int64(), ctypes.c_int64()
