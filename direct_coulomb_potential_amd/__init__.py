@@ -128,6 +128,28 @@ def _stream_ptr(device) -> int:
     return int(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _call(fn_name: str, device, *args):
+    """Call a launching entry point with `device` current and its current
+    stream as the last argument; raise on a non-zero status."""
+    torch = _torch()
+    with torch.cuda.device(device):
+        st = getattr(library(), fn_name)(*args, _stream_ptr(device))
+    _check(fn_name, st)
+
+
+def _buffer(t, dtype, device, name: str, min_numel: int = 0):
+    """Check that t is a contiguous GPU tensor of dtype on device."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda \
+            or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} GPU tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.numel() < min_numel:
+        raise ValueError(f"{name} must have at least {min_numel} elements")
+    return t
+
+
 def _check_atoms(atoms):
     torch = _torch()
     if not isinstance(atoms, torch.Tensor):
@@ -148,6 +170,8 @@ def _out(lat: Lattice, device, out):
     if out.dtype != torch.float32 or not out.is_cuda or not out.is_contiguous() \
             or out.numel() != lat.n_points:
         raise ValueError("out must be a contiguous float32 GPU tensor with nx*ny*nz elements")
+    if out.device != torch.device(device):
+        raise ValueError(f"out is on {out.device}, expected {device}")
     return out
 
 
@@ -172,28 +196,23 @@ def direct(atoms, lat: Lattice, out=None, split: bool = True, workspace=None):
     direct_workspace_bytes() (allocated here unless given as a uint8 GPU
     tensor); split=False calls cpmap_direct.
     """
+    torch = _torch()
     _check_atoms(atoms)
     V = _out(lat, atoms.device, out)
     a_ptr = atoms.data_ptr() if atoms.numel() else None
     v_ptr = V.data_ptr() if V.numel() else None
-    stream = _stream_ptr(atoms.device)
     if not split:
-        st = library().cpmap_direct(a_ptr, atoms.shape[0], *_lat_args(lat), v_ptr, stream)
-        _check("cpmap_direct", st)
+        _call("cpmap_direct", atoms.device, a_ptr, atoms.shape[0], *_lat_args(lat), v_ptr)
         return V
     need = direct_workspace_bytes(atoms.shape[0], lat)
     if workspace is None and need > 0:
-        torch = _torch()
         workspace = torch.empty(need, dtype=torch.uint8, device=atoms.device)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
-        torch = _torch()
-        if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
-            raise ValueError("workspace must be a contiguous uint8 GPU tensor")
+        _buffer(workspace, torch.uint8, atoms.device, "workspace")
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
-    st = library().cpmap_direct_with_workspace(a_ptr, atoms.shape[0], *_lat_args(lat), v_ptr,
-                                               ws_ptr, ws_bytes, stream)
-    _check("cpmap_direct_with_workspace", st)
+    _call("cpmap_direct_with_workspace", atoms.device, a_ptr, atoms.shape[0], *_lat_args(lat),
+          v_ptr, ws_ptr, ws_bytes)
     return V
 
 
@@ -201,11 +220,8 @@ def direct_scatter(atoms, lat: Lattice, out=None):
     """The scatter form of the direct sum (atomics; a contrast, not bit-reproducible)."""
     _check_atoms(atoms)
     V = _out(lat, atoms.device, out)
-    st = library().cpmap_direct_scatter(atoms.data_ptr() if atoms.numel() else None,
-                                        atoms.shape[0], *_lat_args(lat),
-                                        V.data_ptr() if V.numel() else None,
-                                        _stream_ptr(atoms.device))
-    _check("cpmap_direct_scatter", st)
+    _call("cpmap_direct_scatter", atoms.device, atoms.data_ptr() if atoms.numel() else None,
+          atoms.shape[0], *_lat_args(lat), V.data_ptr() if V.numel() else None)
     return V
 
 
@@ -239,13 +255,10 @@ def bin_atoms(atoms, lat: Lattice, bin_size: float, cutoff: float, workspace=Non
     need = bin_workspace_bytes(atoms.shape[0], lat, bin_size, cutoff)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=atoms.device)
-    if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous uint8 GPU tensor")
-    st = library().cpmap_bin_atoms(atoms.data_ptr() if atoms.numel() else None, atoms.shape[0],
-                                   *_lat_args(lat), float(bin_size), float(cutoff),
-                                   workspace.data_ptr(), workspace.numel(),
-                                   _stream_ptr(atoms.device))
-    _check("cpmap_bin_atoms", st)
+    _buffer(workspace, torch.uint8, atoms.device, "workspace")
+    _call("cpmap_bin_atoms", atoms.device, atoms.data_ptr() if atoms.numel() else None,
+          atoms.shape[0], *_lat_args(lat), float(bin_size), float(cutoff),
+          workspace.data_ptr(), workspace.numel())
     return workspace
 
 
@@ -272,11 +285,12 @@ def cutoff(workspace, n_atoms: int, lat: Lattice, bin_size: float, cutoff: float
     """
     if term not in TERMS:
         raise ValueError(f"term must be one of {sorted(TERMS)}")
+    torch = _torch()
+    _buffer(workspace, torch.uint8, workspace.device, "workspace")
     V = _out(lat, workspace.device, out)
-    st = library().cpmap_cutoff_term(workspace.data_ptr(), workspace.numel(), int(n_atoms),
-                                     *_lat_args(lat), float(bin_size), float(cutoff),
-                                     TERMS[term], V.data_ptr(), _stream_ptr(workspace.device))
-    _check("cpmap_cutoff_term", st)
+    _call("cpmap_cutoff_term", workspace.device, workspace.data_ptr(), workspace.numel(),
+          int(n_atoms), *_lat_args(lat), float(bin_size), float(cutoff), TERMS[term],
+          V.data_ptr())
     return V
 
 
@@ -303,17 +317,14 @@ def bin_slots(workspace, n_atoms: int, lat: Lattice, bin_size: float, cutoff: fl
     """Fixed-capacity bins (capacity slots per bin plus an overflow list) from a
     workspace that bin_atoms filled; returns the slot workspace (uint8 tensor)."""
     torch = _torch()
+    _buffer(workspace, torch.uint8, workspace.device, "workspace")
     need = slot_workspace_bytes(n_atoms, lat, bin_size, cutoff, capacity)
     if slot_workspace is None:
         slot_workspace = torch.empty(need, dtype=torch.uint8, device=workspace.device)
-    if slot_workspace.dtype != torch.uint8 or not slot_workspace.is_cuda \
-            or not slot_workspace.is_contiguous():
-        raise ValueError("slot_workspace must be a contiguous uint8 GPU tensor")
-    st = library().cpmap_bin_slots(workspace.data_ptr(), workspace.numel(), int(n_atoms),
-                                   *_lat_args(lat), float(bin_size), float(cutoff),
-                                   int(capacity), slot_workspace.data_ptr(),
-                                   slot_workspace.numel(), _stream_ptr(workspace.device))
-    _check("cpmap_bin_slots", st)
+    _buffer(slot_workspace, torch.uint8, workspace.device, "slot_workspace")
+    _call("cpmap_bin_slots", workspace.device, workspace.data_ptr(), workspace.numel(),
+          int(n_atoms), *_lat_args(lat), float(bin_size), float(cutoff), int(capacity),
+          slot_workspace.data_ptr(), slot_workspace.numel())
     return slot_workspace
 
 
@@ -336,12 +347,12 @@ def cutoff_slots(slot_workspace, n_atoms: int, lat: Lattice, bin_size: float, cu
     """The cutoff sum over fixed-capacity bins (slot pass, then overflow pass)."""
     if term not in TERMS:
         raise ValueError(f"term must be one of {sorted(TERMS)}")
+    torch = _torch()
+    _buffer(slot_workspace, torch.uint8, slot_workspace.device, "slot_workspace")
     V = _out(lat, slot_workspace.device, out)
-    st = library().cpmap_cutoff_slots(slot_workspace.data_ptr(), slot_workspace.numel(),
-                                      int(n_atoms), *_lat_args(lat), float(bin_size),
-                                      float(cutoff), int(capacity), TERMS[term], V.data_ptr(),
-                                      _stream_ptr(slot_workspace.device))
-    _check("cpmap_cutoff_slots", st)
+    _call("cpmap_cutoff_slots", slot_workspace.device, slot_workspace.data_ptr(),
+          slot_workspace.numel(), int(n_atoms), *_lat_args(lat), float(bin_size),
+          float(cutoff), int(capacity), TERMS[term], V.data_ptr())
     return V
 
 
@@ -371,11 +382,15 @@ def extrema(V, workspace=None, out=None):
     need = int(library().cpmap_extrema_workspace_bytes(n))
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=V.device)
-    idx = torch.empty(2, dtype=torch.int64, device=V.device) if out is None else out[0]
-    val = torch.empty(2, dtype=torch.float32, device=V.device) if out is None else out[1]
-    st = library().cpmap_extrema(V.data_ptr() if n else None, n, idx.data_ptr(), val.data_ptr(),
-                                 workspace.data_ptr(), workspace.numel(), _stream_ptr(V.device))
-    _check("cpmap_extrema", st)
+    _buffer(workspace, torch.uint8, V.device, "workspace")
+    if out is None:
+        idx = torch.empty(2, dtype=torch.int64, device=V.device)
+        val = torch.empty(2, dtype=torch.float32, device=V.device)
+    else:
+        idx = _buffer(out[0], torch.int64, V.device, "out[0]", 2)
+        val = _buffer(out[1], torch.float32, V.device, "out[1]", 2)
+    _call("cpmap_extrema", V.device, V.data_ptr() if n else None, n, idx.data_ptr(),
+          val.data_ptr(), workspace.data_ptr(), workspace.numel())
     return idx, val
 
 

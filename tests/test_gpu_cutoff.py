@@ -244,3 +244,33 @@ def test_cutoff_rejects_unknown_term(torch):
     ws = cpmap.bin_atoms(torch.zeros((4, 4), device="cuda"), lat, 1.0, 2.0)
     with pytest.raises(ValueError):
         cpmap.cutoff(ws, 4, lat, 1.0, 2.0, term="hard")
+
+
+def test_binding_rejects_bad_buffers(torch):
+    """Workspaces must be contiguous uint8 GPU tensors and extrema outputs
+    int64/float32 pairs; each wrong buffer is refused before any launch."""
+    lat = Lattice(8, 8, 8, 0.5)
+    atoms = torch.zeros((4, 4), device="cuda")
+    ws = cpmap.bin_atoms(atoms, lat, 1.0, 2.0)
+    with pytest.raises(ValueError):
+        cpmap.cutoff(ws.view(torch.int8), 4, lat, 1.0, 2.0)
+    with pytest.raises(ValueError):
+        cpmap.cutoff(ws.cpu(), 4, lat, 1.0, 2.0)
+    with pytest.raises(ValueError):
+        cpmap.bin_atoms(atoms, lat, 1.0, 2.0, workspace=ws[::2])
+    with pytest.raises(ValueError):
+        cpmap.bin_slots(ws, 4, lat, 1.0, 2.0, 2, slot_workspace=torch.empty(8, device="cuda"))
+    with pytest.raises(ValueError):
+        cpmap.cutoff_slots(ws.view(torch.int8), 4, lat, 1.0, 2.0, 2)
+    with pytest.raises(ValueError):
+        cpmap.direct(atoms, lat, split=True, workspace=torch.empty(64, device="cuda"))
+    V = torch.zeros(lat.n_points, device="cuda")
+    with pytest.raises(ValueError):
+        cpmap.extrema(V, out=(torch.empty(2, dtype=torch.int32, device="cuda"),
+                              torch.empty(2, device="cuda")))
+    with pytest.raises(ValueError):
+        cpmap.extrema(V, out=(torch.empty(1, dtype=torch.int64, device="cuda"),
+                              torch.empty(2, device="cuda")))
+    idx, val = cpmap.extrema(V, out=(torch.empty(2, dtype=torch.int64, device="cuda"),
+                                     torch.empty(2, device="cuda")))
+    assert val.tolist() == [0.0, 0.0]
