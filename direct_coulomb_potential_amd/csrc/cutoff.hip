@@ -22,16 +22,19 @@
 //    into shared memory", one bin at a time there; all spans at once here, in
 //    chunks of kStage atoms, small enough that LDS allows 5 resident waves
 //    per SIMD);
-//  - each wave owns an 8x8x4 slab of the tile and keeps, in an LDS list of
-//    byte offsets into the stage, only the staged atoms within rc of its
-//    slab's node box (one atom per lane tested, ballot + prefix count), which
-//    removes about 40% of the examined pairs at 4 A bins; this is the
-//    lecture's "sphere of bins" idea applied per wave at atom granularity;
-//    atoms within rc of the whole box go to the front of the list and skip
+//  - each wave owns an 8x8x4 half of the tile as four 4x4x4-node cubes of 16
+//    lanes, and each cube keeps, in an LDS list of byte offsets into the
+//    stage, only the staged atoms within rc of its node box (one atom per
+//    lane tested against the four boxes, ballot + prefix count), which
+//    removes about half of the examined pairs at 4 A bins; this is the
+//    lecture's "sphere of bins" idea applied per cube at atom granularity;
+//    atoms within rc of the whole cube go to the front of its list and skip
 //    the cutoff test, the smoothed term's polynomial part of those atoms
 //    coming from their moments (see Moments);
-//  - each lane owns kNx consecutive nodes of one x-row, reads its wave's
-//    listed atoms as LDS broadcasts, shares dy and dz across its nodes, and
+//  - each lane owns kNx consecutive nodes of one x-row and reads its cube's
+//    listed atoms (one LDS address per cube, four per wave read; lists of
+//    unequal length end under an execution mask), shares dy and dz across
+//    its nodes, and
 //    adds the term with r^2 clamped to the largest value <= rc^2 at which the
 //    fp32 term is exactly 0 (found in the prologue; the select-based mask
 //    q -> 0 is the fallback), so atoms beyond the cutoff add exactly nothing
@@ -174,13 +177,15 @@ __host__ __device__ inline bool tile_row(const TileRows &T, int32_t rr, int32_t 
 
 constexpr int kNx = 4;                                 // nodes per lane along x
 constexpr int kThreads = kTile * kTile * kTile / kNx;  // 128
-constexpr int kStage = 512;                            // atoms staged per chunk (8 KB)
+constexpr int kCube = 4;                               // a list group's cube of nodes
+constexpr int kGroupLanes = kCube * kCube * kCube / kNx;  // 16 lanes per cube
+constexpr int kGroups = 64 / kGroupLanes;              // 4 cubes per wave
+constexpr int kStage = 256;                            // atoms staged per chunk (4 KB)
 constexpr int kMaxRows = 256;                          // (cy, cz) rows per list chunk
 // Resident waves per SIMD the kernel is built for: the sweep is latency-bound
 // on its LDS reads below this (measured 1.74 ms at 4 waves, 1.66 ms at 5 on
-// the 100k-atom rc = 12 A map); at 5 the register budget is 102 VGPRs and the
-// few spills the compiler adds sit outside the sweep loops.  LDS per
-// workgroup (about 15 KB) allows 5 as well.
+// the 100k-atom rc = 12 A map).  LDS per workgroup (about 14 KB: the stage
+// and eight lists of kStage entries) allows 5 as well.
 constexpr int kWavesPerSimd = 5;
 
 // kRsqInside serves atoms within the cutoff of every node of the wave, which
@@ -307,14 +312,21 @@ __device__ __forceinline__ void moments_add(Moments &M, const float4 at, const f
     M.s4 = fmaf(qs, s, M.s4);
 }
 
-// Sum over the wave's 64 lanes by an xor butterfly: both partners of a step
-// add the same two values, so every lane ends with the same total.
+// Sum over a cube's kGroupLanes lanes by an xor butterfly: both partners of
+// a step add the same two values, so every lane ends with the same total.
 __device__ __forceinline__ float wave_sum(float v)
 {
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1)
+    for (int m = kGroupLanes / 2; m >= 1; m >>= 1)
         v += __shfl_xor(v, m);
     return v;
+}
+
+// Number of lanes below this one whose bit is set in mask.
+__device__ __forceinline__ int32_t lanes_below(uint64_t mask)
+{
+    return (int32_t)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                              __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
 __device__ __forceinline__ void moments_reduce(Moments &M)
@@ -386,7 +398,7 @@ cutoff_kernel(CutoffParams P0, const int32_t *__restrict__ bin_start,
               const float4 *__restrict__ sorted, int32_t n_sorted, float *__restrict__ V)
 {
     __shared__ float4 stage[kStage];
-    __shared__ uint32_t wave_list[kWaves][kStage];  // byte offsets into stage
+    __shared__ uint32_t cube_list[kWaves][kGroups][kStage];  // byte offsets into stage
     __shared__ int32_t span_src[kMaxRows];
     __shared__ int32_t span_off[kMaxRows + 1];
     __shared__ int32_t wave_total[kWaves];
@@ -417,21 +429,22 @@ cutoff_kernel(CutoffParams P0, const int32_t *__restrict__ bin_start,
         T = tile_rows(tx, ty, tz, P.n, P.h, P.o, P.b0, P.nb, P.bs, P.list_rc);
     __syncthreads();
 
-    // This lane's nodes: an x-run of kNx nodes in one row of one plane; the
-    // wave's 64 lanes cover 8 x 8 x (kTile / kWaves) nodes.
-    const int32_t xs = t % (kTile / kNx);
-    const int32_t yl = (t / (kTile / kNx)) % kTile;
-    const int32_t zl = t / (kTile / kNx * kTile);
-    const int32_t i0 = tx * kTile + xs * kNx;
-    const int32_t j = ty * kTile + yl;
-    const int32_t k = tz * kTile + zl;
+    // This lane's nodes: an x-run of kNx nodes.  Wave w covers the tile's
+    // z-half w (8 x 8 x 4 nodes) as four 4 x 4 x 4-node cubes, 16 lanes each:
+    // cube q of the wave takes x-half q & 1 and y-half q >> 1, and its lanes
+    // the cube's 4 x 4 (y, z) rows.  Each cube keeps its own atom list.
+    const int q = lane / kGroupLanes;
+    const int ql = lane % kGroupLanes;
+    const int32_t i0 = tx * kTile + (q & 1) * kCube;
+    const int32_t j = ty * kTile + (q >> 1) * kCube + ql % kCube;
+    const int32_t k = tz * kTile + wave * kCube + ql / kCube;
     float x[kNx];
 #pragma unroll
     for (int c = 0; c < kNx; ++c)
         x[c] = node_coord(i0 + c, P.h, P.o[0]);
     const float y = node_coord(j, P.h, P.o[1]);
     const float z = node_coord(k, P.h, P.o[2]);
-    // atoms inside the cutoff of the whole wave and boundary atoms are summed
+    // atoms inside the cutoff of the whole cube and boundary atoms are summed
     // apart (each in staged order), so the order does not depend on chunking
     float acc_in[kNx], acc_bd[kNx];
 #pragma unroll
@@ -439,30 +452,35 @@ cutoff_kernel(CutoffParams P0, const int32_t *__restrict__ bin_start,
         acc_in[c] = 0.0f;
         acc_bd[c] = 0.0f;
     }
-    // the smoothed term's polynomial part over the inside atoms, from their
-    // moments about the wave's centre: lane l accumulates the tile's inside
-    // atoms number l, l + 64, ... (counted in staged order over all chunks)
+    // the smoothed term's polynomial part over the cube's inside atoms, from
+    // their moments about the wave's centre: lane l of the cube accumulates
+    // the cube's inside atoms number l, l + 16, ... (counted in staged order
+    // over all chunks)
     Moments mom;
     moments_zero(mom);
     int32_t inside_seen = 0;
 
-    // The wave's node box (nodes past the lattice edge included: they are
-    // computed and dropped, so the box only needs to contain the live ones).
-    constexpr int kSlab = kTile / kWaves;
-    const float wlo[3] = {node_coord((int64_t)tx * kTile, P.h, P.o[0]),
-                          node_coord((int64_t)ty * kTile, P.h, P.o[1]),
-                          node_coord((int64_t)tz * kTile + wave * kSlab, P.h, P.o[2])};
-    const float whi[3] = {node_coord((int64_t)tx * kTile + kTile - 1, P.h, P.o[0]),
-                          node_coord((int64_t)ty * kTile + kTile - 1, P.h, P.o[1]),
-                          node_coord((int64_t)tz * kTile + wave * kSlab + kSlab - 1, P.h,
-                                     P.o[2])};
-    // a slightly widened radius keeps the list conservative against rounding;
-    // a slightly narrowed one keeps "inside" safely inside (r^2 below the
-    // clamp value or rc^2 at every node of the wave)
+    // The cubes' node boxes (nodes past the lattice edge included: they are
+    // computed and dropped, so a box only needs to contain the live ones).
+    // Both x-halves, both y-halves and the wave's z-range; the same for the
+    // whole wave.
+    const int64_t nx0 = (int64_t)tx * kTile, ny0 = (int64_t)ty * kTile;
+    const int64_t nz0 = (int64_t)tz * kTile + wave * kCube;
+    const float cxlo[2] = {node_coord(nx0, P.h, P.o[0]), node_coord(nx0 + kCube, P.h, P.o[0])};
+    const float cxhi[2] = {node_coord(nx0 + kCube - 1, P.h, P.o[0]),
+                           node_coord(nx0 + kTile - 1, P.h, P.o[0])};
+    const float cylo[2] = {node_coord(ny0, P.h, P.o[1]), node_coord(ny0 + kCube, P.h, P.o[1])};
+    const float cyhi[2] = {node_coord(ny0 + kCube - 1, P.h, P.o[1]),
+                           node_coord(ny0 + kTile - 1, P.h, P.o[1])};
+    const float czlo = node_coord(nz0, P.h, P.o[2]);
+    const float czhi = node_coord(nz0 + kCube - 1, P.h, P.o[2]);
+    // a slightly widened radius keeps the lists conservative against
+    // rounding; a slightly narrowed one keeps "inside" safely inside (r^2
+    // below the clamp value or rc^2 at every node of the cube)
     const float keep2 = P0.rc2 * 1.0001f;
     const float inside2 = P.rc2 * 0.9999f;
-    const float centre[3] = {0.5f * (wlo[0] + whi[0]), 0.5f * (wlo[1] + whi[1]),
-                             0.5f * (wlo[2] + whi[2])};
+    const float centre[3] = {0.5f * (cxlo[0] + cxhi[1]), 0.5f * (cylo[0] + cyhi[1]),
+                             0.5f * (czlo + czhi)};
     bool any_atoms = false;
 
     for (int32_t row0 = 0; row0 < T.nrows; row0 += kMaxRows) {
@@ -544,54 +562,101 @@ cutoff_kernel(CutoffParams P0, const int32_t *__restrict__ bin_start,
                 stage[e] = sorted[span_src[a] + (g - span_off[a])];
             }
             __syncthreads();
-            // inside atoms fill the list from the front, boundary atoms from
-            // the back; together they are at most m <= kStage entries
-            int32_t n_in = 0, n_bd = 0;
+            // each cube's list: inside atoms from the front, boundary atoms
+            // from the back; together at most m <= kStage entries
+            int32_t n_in[kGroups], n_bd[kGroups];
+#pragma unroll
+            for (int g = 0; g < kGroups; ++g)
+                n_in[g] = n_bd[g] = 0;
             for (int32_t e0 = 0; e0 < m; e0 += 64) {
                 const int32_t e = e0 + lane;
-                bool near = false, inside = false;
+                bool near[kGroups], inside[kGroups];
+#pragma unroll
+                for (int g = 0; g < kGroups; ++g)
+                    near[g] = inside[g] = false;
                 if (e < m) {
                     const float4 at = stage[e];
-                    const float gx = fmaxf(fmaxf(wlo[0] - at.x, at.x - whi[0]), 0.0f);
-                    const float gy = fmaxf(fmaxf(wlo[1] - at.y, at.y - whi[1]), 0.0f);
-                    const float gz = fmaxf(fmaxf(wlo[2] - at.z, at.z - whi[2]), 0.0f);
-                    near = fmaf(gx, gx, fmaf(gy, gy, gz * gz)) < keep2;
-                    // distance to the farthest corner of the wave's box
-                    const float fx = fmaxf(at.x - wlo[0], whi[0] - at.x);
-                    const float fy = fmaxf(at.y - wlo[1], whi[1] - at.y);
-                    const float fz = fmaxf(at.z - wlo[2], whi[2] - at.z);
-                    inside = near && fmaf(fx, fx, fmaf(fy, fy, fz * fz)) < inside2;
+                    // per axis and half: squared gap to the box (0 inside
+                    // it) and squared distance to its far face
+                    float gx[2], fx[2], gy[2], fy[2];
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const float lx = cxlo[hh] - at.x, ux = at.x - cxhi[hh];
+                        const float ly = cylo[hh] - at.y, uy = at.y - cyhi[hh];
+                        const float ax = fmaxf(fmaxf(lx, ux), 0.0f), bx = fmaxf(-lx, -ux);
+                        const float ay = fmaxf(fmaxf(ly, uy), 0.0f), by = fmaxf(-ly, -uy);
+                        gx[hh] = ax * ax;
+                        fx[hh] = bx * bx;
+                        gy[hh] = ay;
+                        fy[hh] = by;
+                    }
+                    const float lz = czlo - at.z, uz = at.z - czhi;
+                    const float az = fmaxf(fmaxf(lz, uz), 0.0f), bz = fmaxf(-lz, -uz);
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const float gyz = fmaf(gy[hh], gy[hh], az * az);
+                        const float fyz = fmaf(fy[hh], fy[hh], bz * bz);
+#pragma unroll
+                        for (int xh = 0; xh < 2; ++xh) {
+                            const int g = 2 * hh + xh;
+                            near[g] = gx[xh] + gyz < keep2;
+                            inside[g] = near[g] && fx[xh] + fyz < inside2;
+                        }
+                    }
                 }
-                const uint64_t v_in = __ballot(inside);
-                const uint64_t v_bd = __ballot(near && !inside);
-                const uint64_t lower = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-                if (inside)
-                    wave_list[wave][n_in + __popcll(v_in & lower)] = (uint32_t)e * 16u;
-                else if (near)
-                    wave_list[wave][kStage - 1 - (n_bd + __popcll(v_bd & lower))] =
-                        (uint32_t)e * 16u;
-                n_in += __popcll(v_in);
-                n_bd += __popcll(v_bd);
+#pragma unroll
+                for (int g = 0; g < kGroups; ++g) {
+                    const uint64_t v_in = __ballot(inside[g]);
+                    const uint64_t v_bd = __ballot(near[g] && !inside[g]);
+                    if ((v_in | v_bd) == 0)
+                        continue;
+                    uint32_t *list = cube_list[wave][g];
+                    if (inside[g])
+                        list[n_in[g] + lanes_below(v_in)] = (uint32_t)e * 16u;
+                    else if (near[g])
+                        list[kStage - 1 - (n_bd[g] + lanes_below(v_bd))] = (uint32_t)e * 16u;
+                    n_in[g] += __popcll(v_in);
+                    n_bd[g] += __popcll(v_bd);
+                }
             }
-            n_in = __builtin_amdgcn_readfirstlane(n_in);
-            n_bd = __builtin_amdgcn_readfirstlane(n_bd);
-            // the list is written and read by this wave only
+            // the lists are written and read by this wave only
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            const uint32_t *front = wave_list[wave];
-            const uint32_t *back = wave_list[wave] + (kStage - 1);
-            sweep<kRsqInside, 1>(stage, front, n_in, x, y, z, P, acc_in);
+            // every lane sweeps its cube's list; the lists' common length
+            // without masks, the rest with the lanes whose list is longer
+            int32_t my_in = n_in[0], my_bd = n_bd[0];
+            int32_t min_in = n_in[0], min_bd = n_bd[0];
+#pragma unroll
+            for (int g = 1; g < kGroups; ++g) {
+                my_in = q == g ? n_in[g] : my_in;
+                my_bd = q == g ? n_bd[g] : my_bd;
+                min_in = n_in[g] < min_in ? n_in[g] : min_in;
+                min_bd = n_bd[g] < min_bd ? n_bd[g] : min_bd;
+            }
+            const uint32_t *front = cube_list[wave][q];
+            const uint32_t *back = front + (kStage - 1);
+            sweep<kRsqInside, 1>(stage, front, min_in, x, y, z, P, acc_in);
+            for (int32_t i = min_in; i < my_in; ++i)
+                add_atom<kRsqInside>(staged(stage, front[i]), x, y, z, P, acc_in);
             if (mode == kTruncated) {
-                sweep<kTruncated, -1>(stage, back, n_bd, x, y, z, P, acc_bd);
+                sweep<kTruncated, -1>(stage, back, min_bd, x, y, z, P, acc_bd);
+                for (int32_t i = min_bd; i < my_bd; ++i)
+                    add_atom<kTruncated>(staged(stage, back[-i]), x, y, z, P, acc_bd);
             } else {
-                for (int32_t i = (lane - inside_seen) & 63; i < n_in; i += 64)
+                for (int32_t i = (ql - inside_seen) & (kGroupLanes - 1); i < my_in;
+                     i += kGroupLanes)
                     moments_add(mom, staged(stage, front[i]), centre);
-                inside_seen += n_in;
-                if (mode == kSmoothClamp)
-                    sweep<kSmoothClamp, -1>(stage, back, n_bd, x, y, z, P, acc_bd);
-                else
-                    sweep<kSmoothSelect, -1>(stage, back, n_bd, x, y, z, P, acc_bd);
+                inside_seen += my_in;
+                if (mode == kSmoothClamp) {
+                    sweep<kSmoothClamp, -1>(stage, back, min_bd, x, y, z, P, acc_bd);
+                    for (int32_t i = min_bd; i < my_bd; ++i)
+                        add_atom<kSmoothClamp>(staged(stage, back[-i]), x, y, z, P, acc_bd);
+                } else {
+                    sweep<kSmoothSelect, -1>(stage, back, min_bd, x, y, z, P, acc_bd);
+                    for (int32_t i = min_bd; i < my_bd; ++i)
+                        add_atom<kSmoothSelect>(staged(stage, back[-i]), x, y, z, P, acc_bd);
+                }
             }
             __syncthreads();
         }
@@ -609,9 +674,10 @@ cutoff_kernel(CutoffParams P0, const int32_t *__restrict__ bin_start,
     // the sweep (the empty asm keeps the compiler from reusing the early ones).
     int32_t te = threadIdx.x;
     asm volatile("" : "+v"(te));
-    const int32_t i0s = tx * kTile + (te % (kTile / kNx)) * kNx;
-    const int32_t js = ty * kTile + (te / (kTile / kNx)) % kTile;
-    const int32_t ks = tz * kTile + te / (kTile / kNx * kTile);
+    const int32_t qs = (te % 64) / kGroupLanes, ls = te % kGroupLanes;
+    const int32_t i0s = tx * kTile + (qs & 1) * kCube;
+    const int32_t js = ty * kTile + (qs >> 1) * kCube + ls % kCube;
+    const int32_t ks = tz * kTile + (te / 64) * kCube + ls / kCube;
     if (js >= P.n[1] || ks >= P.n[2])
         return;
     float *out = V + ((int64_t)ks * P.n[1] + js) * P.n[0];
