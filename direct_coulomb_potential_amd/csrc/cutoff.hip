@@ -43,7 +43,7 @@
 //
 // The same kernel walks fixed-capacity bins (the lecture's slides 33-35): a
 // run of bins is then a run of cap-slot blocks, whose span follows from the
-// geometry alone, and empty slots (at +inf) never pass the per-wave list
+// geometry alone, and empty slots (at +inf) never pass the per-cube list
 // test.  The bins' overflow is a CSR of its own; a second launch walks it and
 // adds into V, skipping tiles whose neighbourhood holds no overflow atom.
 #include <cmath>
@@ -545,8 +545,8 @@ cutoff_kernel(CutoffParams P0, const int32_t *__restrict__ bin_start,
         any_atoms |= total > 0;
         __syncthreads();
 
-        // 3. stage the spans' atoms in chunks; each wave lists the atoms near
-        //    its slab and sweeps them
+        // 3. stage the spans' atoms in chunks; each cube lists the atoms near
+        //    its nodes and its lanes sweep them
         for (int32_t c0 = 0; c0 < total; c0 += kStage) {
             const int32_t m = total - c0 < kStage ? total - c0 : kStage;
             for (int32_t e = t; e < m; e += kThreads) {
