@@ -143,6 +143,31 @@ def test_cutoff_no_atoms(torch):
     assert torch.all(V == 0).item()
 
 
+# Cutoffs for which, on gfx950, no r^2 within 64 ulps below fl(rc*rc) makes
+# the fp32 smoothed term exactly 0 (found with a probe of that search using
+# the hardware rsq), so the kernel sums with its compare-and-select mask
+# instead of the r^2 clamp; 12.0 takes the clamp.  The parity bar is the
+# same either way.
+FALLBACK_CUTOFFS = [1.02, 11.91, 12.55, 12.0]
+
+
+@pytest.mark.parametrize("rc", FALLBACK_CUTOFFS)
+def test_cutoff_select_and_clamp_cutoffs_all_nodes(torch, rc):
+    print(f"[cutoff select/clamp] rc={rc}", flush=True)
+    bs = rc / 3.0
+    lat = Lattice(26, 22, 18, 0.5, (0.5, -1.0, 2.0))
+    lo = np.array(lat.origin) - rc
+    hi = np.array(lat.origin) + np.array(lat.dims) * lat.spacing + rc
+    n = 3000
+    atoms_np = wl.random_atoms(n, lo, hi, seed=int(rc * 100))
+    atoms = torch.from_numpy(atoms_np).cuda()
+    ws = cpmap.bin_atoms(atoms, lat, bs, rc)
+    V = cpmap.cutoff(ws, n, lat, bs, rc).cpu().numpy().reshape(-1)
+    Vo, S = oracle.cutoff(atoms_np, lat.dims, lat.spacing, lat.origin, rc, with_scale=True)
+    _parity(V, Vo, S, f"rc={rc}")
+    assert np.all(V[S == 0] == 0.0)
+
+
 def test_cutoff_config5_checked_nodes(torch):
     w = wl.cutoff_binned()
     lat = w.lattice
