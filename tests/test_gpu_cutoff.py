@@ -251,6 +251,28 @@ def test_truncated_boundary_decisions(torch):
     _parity(V, Vo, S, "truncated boundary")
 
 
+# Atoms around a node at the origin, rc = 3, for which the fp32 inclusion
+# chain and the exact distance disagree (the oracle pins re-derive this in
+# exact arithmetic): the first is dropped, the second kept.
+FP32_SPLIT_ATOMS = [((-0.1108543872833252, -1.9783434867858887, 2.2525248527526855), False),
+                    ((-0.15722495317459106, 0.6464439630508423, 2.9253017902374268), True)]
+
+
+@pytest.mark.parametrize("atom,kept", FP32_SPLIT_ATOMS, ids=["dropped", "kept"])
+@pytest.mark.parametrize("bs", [1.0, 1.5, 4.0])
+def test_truncated_decision_matches_oracle_where_exact_distance_disagrees(torch, atom, kept, bs):
+    print(f"[truncated fp32 split] kept={kept} bs={bs}", flush=True)
+    atoms_np = np.array([[*atom, 0.75]], dtype=np.float32)
+    lat = Lattice(1, 1, 1, 1.0)
+    ws = cpmap.bin_atoms(torch.from_numpy(atoms_np).cuda(), lat, bs, 3.0)
+    V = cpmap.cutoff(ws, 1, lat, bs, 3.0, term="truncated").cpu().numpy().reshape(-1)
+    Vo = oracle.cutoff_hard(atoms_np, lat.dims, lat.spacing, lat.origin, 3.0)
+    if kept:
+        assert Vo[0] != 0.0 and abs(V[0] - Vo[0]) <= 1e-5 * abs(Vo[0])
+    else:
+        assert Vo[0] == 0.0 and V[0] == 0.0
+
+
 def test_truncated_config5_checked_nodes(torch):
     w = wl.cutoff_binned()
     lat = w.lattice

@@ -412,6 +412,57 @@ def test_cutoff_hard_decision_is_taken_in_fp32():
     assert Vo[0] == 0.0
 
 
+# Atoms around a node at the origin, rc = 3, for which R14's fp32 chain and
+# the exact distance decide differently (found by a search in exact rational
+# arithmetic; the test re-derives the disagreement before relying on it).
+FP32_SPLIT_ATOMS = {
+    # exact r^2 = 9 - 1.4e-7 < 9, but the fp32 chain rounds r^2 to 9.0
+    "kept_exactly_dropped_in_fp32": (-0.1108543872833252, -1.9783434867858887,
+                                     2.2525248527526855),
+    # exact r^2 = 9 + 4.7e-8 >= 9, but the fp32 chain gives 8.999999
+    "dropped_exactly_kept_in_fp32": (-0.15722495317459106, 0.6464439630508423,
+                                     2.9253017902374268),
+}
+
+
+def _round_f32(fr):
+    """The fp32 value nearest to the rational fr (ties to even)."""
+    f = np.float32(float(fr))
+    cands = [np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))]
+    return min(cands, key=lambda c: (abs(Fraction(float(c)) - fr),
+                                     int(np.array(c, np.float32).view(np.uint32)) & 1))
+
+
+def _fp32_chain_r2(dx, dy, dz):
+    """fma(dx, dx, fma(dy, dy, fl(dz*dz))), every step one rounding of its
+    exact value."""
+    def fr(v):
+        return Fraction(float(v))
+    dz2 = _round_f32(fr(dz) ** 2)
+    t = _round_f32(fr(dy) * fr(dy) + fr(dz2))
+    return _round_f32(fr(dx) * fr(dx) + fr(t))
+
+
+@pytest.mark.parametrize("case", sorted(FP32_SPLIT_ATOMS))
+def test_cutoff_hard_follows_fp32_where_the_exact_distance_disagrees(case):
+    """Reading R14 decides inclusion in fp32: an atom the exact distance
+    keeps but the fp32 chain rounds to rc^2 is dropped, and one the exact
+    distance drops but the fp32 chain puts below rc^2 is kept (V = q/r with
+    r within 1e-7 of rc)."""
+    a = np.array(FP32_SPLIT_ATOMS[case], dtype=np.float32)
+    d = -a  # node at the origin: node - atom, exact in fp32
+    kept_exact = sum(Fraction(float(v)) ** 2 for v in d) < 9
+    kept_fp32 = bool(_fp32_chain_r2(*d) < np.float32(9.0))
+    assert kept_fp32 != kept_exact
+    assert kept_fp32 == (case == "dropped_exactly_kept_in_fp32")
+    atoms = np.array([[*a, 0.75]], dtype=np.float32)
+    V, S = oracle.cutoff_hard(atoms, (1, 1, 1), 1.0, (0.0, 0.0, 0.0), 3.0, with_scale=True)
+    if kept_fp32:
+        assert V[0] == pytest.approx(0.25, rel=1e-7) and S[0] == pytest.approx(0.25, rel=1e-7)
+    else:
+        assert V[0] == 0.0 and S[0] == 0.0
+
+
 def test_cutoff_hard_with_huge_cutoff_is_the_direct_sum():
     """With rc beyond every distance every atom is kept, and the kept terms
     are summed exactly as the direct sum sums them: bit-identical results."""
