@@ -185,6 +185,26 @@ def test_binding_rejects_cpu_and_wrong_dtype_tensors():
         cpmap.direct([[0, 0, 0, 1]], Lattice(2, 2, 2, 0.5))
 
 
+def test_binding_rejects_host_buffers_before_any_launch():
+    """Workspaces and outputs are checked (dtype, GPU, contiguity) before the
+    library is asked to launch anything."""
+    torch = pytest.importorskip("torch")
+    lat = Lattice(8, 8, 8, 0.5)
+    host_ws = torch.zeros(1 << 16, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        cpmap.cutoff(host_ws, 4, lat, 1.0, 2.0)
+    with pytest.raises(ValueError):
+        cpmap.cutoff(host_ws.view(torch.int8), 4, lat, 1.0, 2.0)
+    with pytest.raises(ValueError):
+        cpmap.cutoff_slots(host_ws, 4, lat, 1.0, 2.0, 2)
+    with pytest.raises(ValueError):
+        cpmap.bin_slots(host_ws, 4, lat, 1.0, 2.0, 2)
+    with pytest.raises(ValueError):
+        cpmap.extrema(torch.zeros(16))
+    with pytest.raises(ValueError):
+        cpmap.cutoff(host_ws, 4, lat, 1.0, 2.0, term="hard")
+
+
 def test_direct_workspace_queries_and_checks():
     lib = cpmap.library()
     need = lib.cpmap_direct_workspace_bytes(200_000, 200, 200, 200)
