@@ -205,6 +205,17 @@ def test_binding_rejects_host_buffers_before_any_launch():
         cpmap.cutoff(host_ws, 4, lat, 1.0, 2.0, term="hard")
 
 
+def test_planner_picks_each_variant_for_its_test_geometry():
+    """The GPU test that runs every compiled direct variant relies on these
+    choices; a planner change that moves a geometry to another variant shows
+    here first."""
+    from test_gpu_direct import VARIANT_CASES
+    for variant, n, dims, split in VARIANT_CASES:
+        lat = Lattice(*dims, 0.5, (-1.25, 0.5, 2.0))
+        assert cpmap.direct_plan(n, lat, split)[:4] == variant, (variant, n, dims)
+    assert len({c[0] for c in VARIANT_CASES}) == 9
+
+
 def test_direct_workspace_queries_and_checks():
     lib = cpmap.library()
     need = lib.cpmap_direct_workspace_bytes(200_000, 200, 200, 200)

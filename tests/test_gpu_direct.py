@@ -92,6 +92,36 @@ def test_direct_zero_charges_and_far_atoms(torch):
     _assert_parity(Vg2, Vo2, S, "zero charges removed")
 
 
+# One geometry per compiled kernel variant (nodes per lane x, y, z; waves per
+# workgroup), each with ragged lattice edges; the planner's choice for each
+# is pinned on the CPU in test_abi.py.
+VARIANT_CASES = [
+    ((8, 8, 2, 4), 8000, (97, 5, 151), True),
+    ((8, 8, 2, 8), 8000, (97, 73, 15), True),
+    ((8, 4, 2, 4), 8000, (13, 73, 47), True),
+    ((8, 4, 2, 8), 300, (57, 57, 151), True),
+    ((4, 4, 2, 8), 8000, (3, 37, 151), True),
+    ((4, 4, 2, 16), 300, (41, 37, 151), True),
+    ((4, 4, 1, 16), 300, (97, 19, 67), True),
+    ((2, 2, 1, 16), 300, (65, 11, 23), True),
+    ((1, 1, 1, 16), 300, (3, 5, 1), True),
+]
+
+
+@pytest.mark.parametrize("variant,n,dims,split", VARIANT_CASES,
+                         ids=["x".join(map(str, c[0])) for c in VARIANT_CASES])
+def test_direct_each_compiled_variant_all_nodes(torch, variant, n, dims, split):
+    lat = Lattice(*dims, 0.5, (-1.25, 0.5, 2.0))
+    plan = cpmap.direct_plan(n, lat, split)
+    print(f"[direct variant] {variant} n={n} dims={dims} plan={plan}", flush=True)
+    lo = np.array(lat.origin) - 5.0
+    hi = np.array(lat.origin) + np.array(dims) * lat.spacing + 5.0
+    atoms = wl.random_atoms(n, lo, hi, seed=sum(dims) + n)
+    Vg = _run_direct(torch, atoms, lat, split)
+    Vo, S = oracle.direct(atoms, lat.dims, lat.spacing, lat.origin, with_scale=True)
+    _assert_parity(Vg, Vo, S, f"variant {variant}")
+
+
 @pytest.mark.parametrize("split", [False, True], ids=["plain", "split"])
 def test_direct_same_sign_charges_large_n(torch, split):
     """All-positive charges over many atoms: the blocked fp32 sum must stay
