@@ -20,7 +20,7 @@ from direct_coulomb_potential_amd import workloads as wl
 pytestmark = pytest.mark.gpu
 
 TOL = 1e-5
-N_CASES = 120
+N_CASES = 400
 
 
 @pytest.fixture(scope="module")
