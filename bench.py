@@ -1,8 +1,9 @@
 """Benchmark of the potential-map hot path on one MI355X.
 
-One step = one cpmap_direct call over the 200^3 lattice (0.5 A) with 200,000
-uniform atoms (charges U[-1,1] shifted to net zero): 1.6e12 atom-node
-evaluations.  After the timed direct steps the same run times the cutoff path
+One step = one direct-sum call (cpmap_direct_with_workspace: atoms also split
+across workgroups into partial maps) over the 200^3 lattice (0.5 A) with
+200,000 uniform atoms (charges U[-1,1] shifted to net zero): 1.6e12
+atom-node evaluations.  After the timed direct steps the same run times the cutoff path
 (cpmap_bin_atoms + cpmap_cutoff) on the 100k-atom, rc = 12 A, 4 A-bin system
 over the same lattice and reports it beside the headline number.
 
