@@ -24,7 +24,8 @@
  *     returns a status and enqueues nothing.  Device data is not inspected:
  *     an atom placed exactly on a node gives an infinite potential there, and
  *     non-finite atom data propagates into V.
- *   - Results are deterministic: the same inputs give bit-identical outputs.
+ *   - Results are deterministic: the same inputs give bit-identical outputs
+ *     (except cpmap_direct_scatter, the atomics contrast, as stated there).
  */
 #ifndef CPMAP_H
 #define CPMAP_H
