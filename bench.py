@@ -221,6 +221,9 @@ def main():
             "clock_ghz_measured": clock,
             "frac_at_measured_clock": (achieved / (PEAK_FP32_TFLOPS * clock / PEAK_CLOCK_GHZ)
                                        if clock else None),
+            # rocprof's VALUBusy from the committed counters (>= 100: every
+            # SIMD's VALU issue saturated; null once the source has changed)
+            "valu_busy_pct_from_counters": prof.get("valu_busy_pct") if prof else None,
         }
         # ion placement on the map just computed: argmin / argmax over 8M nodes
         ext_ws = torch.empty(cpmap.library().cpmap_extrema_workspace_bytes(lat.n_points),
@@ -434,6 +437,11 @@ def bench_cutoff(torch, cpmap, wl, dev, args):
         "in_cutoff_G_pairs_per_s": in_cut / (cut_ms * 1e-3) / 1e9,
         "evaluated_pairs_from_counters": examined,
         "evaluated_G_pairs_per_s": examined / (cut_ms * 1e-3) / 1e9 if examined else None,
+        # the cutoff kernel is VALU-bound too: rocprof's VALUBusy from the
+        # committed counters (null once the source has changed)
+        "valu_busy_pct_from_counters": prof.get("valu_busy_pct") if prof else None,
+        "hbm_traffic_gbs_from_counters": (prof["traffic_bytes_per_launch"] / (cut_ms * 1e-3) / 1e9
+                                          if prof else None),
     }
     if not args.no_cpu_baseline:
         import oracle
