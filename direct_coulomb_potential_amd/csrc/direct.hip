@@ -146,13 +146,38 @@ __global__ __launch_bounds__(kWave *W) void direct_kernel(
         }
         for (; a < hi; ++a)
             accumulate_atom<CX, CY, CZ>(atoms[a], x, y, z, acc);
-        // Add the round's partial sums into the LDS total in wave order.
-        for (int w = 0; w < W; ++w) {
-            __syncthreads();
-            if (slice == w) {
+        // Add the round's partial sums into the LDS total.  Up to 8 waves:
+        // the nodes are cut into W chunks and in phase s wave w adds its
+        // chunk (w + s) mod W, so the waves update disjoint chunks at once
+        // and chunk c receives the waves in the fixed order c, c - 1, ...
+        // (mod W).  16 waves (1 to 32 nodes per lane): one wave after the
+        // other, in wave order; rotating there costs scalar registers and
+        // halves those variants' occupancy.
+        if constexpr (W <= 8) {
+            constexpr int kPer = (NP + W - 1) / W;
+            for (int s = 0; s < W; ++s) {
+                __syncthreads();
+                const int mine = (slice + s) % W;
 #pragma unroll
-                for (int p = 0; p < NP; ++p)
-                    total[p * kWave + lane] += acc[p];
+                for (int c = 0; c < W; ++c) {
+                    if (c != mine)
+                        continue;
+#pragma unroll
+                    for (int i = 0; i < kPer; ++i) {
+                        const int p = c * kPer + i;
+                        if (p < NP)
+                            total[p * kWave + lane] += acc[p];
+                    }
+                }
+            }
+        } else {
+            for (int w = 0; w < W; ++w) {
+                __syncthreads();
+                if (slice == w) {
+#pragma unroll
+                    for (int p = 0; p < NP; ++p)
+                        total[p * kWave + lane] += acc[p];
+                }
             }
         }
     }
@@ -207,8 +232,9 @@ struct Variant {
 
 #define CPMAP_VARIANT(CX, CY, CZ, W, OCC) Variant{CX, CY, CZ, W, OCC, direct_kernel<CX, CY, CZ, W>}
 
-// Occupancies are those of the gfx950 build (189, 117, 69, 54, 41 and 29
-// VGPRs; LDS never limits); a GPU test checks them against the runtime.
+// Occupancies (resident waves per SIMD) are those of the gfx950 build (183,
+// 111, 67, 54, 41 and 29 VGPRs; LDS never limits); a GPU test checks them
+// against the runtime.
 const Variant kVariants[] = {
     CPMAP_VARIANT(8, 8, 2, 4, 2),  CPMAP_VARIANT(8, 8, 2, 8, 2),  CPMAP_VARIANT(8, 4, 2, 4, 4),
     CPMAP_VARIANT(8, 4, 2, 8, 4),  CPMAP_VARIANT(4, 4, 2, 8, 6),  CPMAP_VARIANT(4, 4, 2, 16, 4),
