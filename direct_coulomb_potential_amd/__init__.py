@@ -37,6 +37,8 @@ STATUS = {0: "CPMAP_OK", 1: "CPMAP_EINVAL", 2: "CPMAP_ERANGE", 3: "CPMAP_ENOSPC"
 
 
 class CpmapError(RuntimeError):
+    """A cpmap_status other than CPMAP_OK; `status` holds its code."""
+
     def __init__(self, fn: str, status: int, msg: str):
         super().__init__(f"{fn}: {STATUS.get(status, status)} ({msg})")
         self.status = status
@@ -77,6 +79,7 @@ _SIGNATURES = {
 
 
 def library_path() -> str:
+    """Path of the libcpmap.so this binding loads (next to this file)."""
     return _LIB_PATH
 
 
@@ -226,6 +229,8 @@ def direct_scatter(atoms, lat: Lattice, out=None):
 
 
 def bin_workspace_bytes(n_atoms: int, lat: Lattice, bin_size: float, cutoff: float) -> int:
+    """Bytes of the workspace bin_atoms fills for this atom count and geometry
+    (cpmap_bin_workspace_bytes); raises CpmapError for an invalid geometry."""
     n = library().cpmap_bin_workspace_bytes(int(n_atoms), *_lat_args(lat), float(bin_size),
                                             float(cutoff))
     if n == 0:
@@ -234,6 +239,7 @@ def bin_workspace_bytes(n_atoms: int, lat: Lattice, bin_size: float, cutoff: flo
 
 
 def bin_grid(lat: Lattice, bin_size: float, cutoff: float) -> Tuple[int, int, int]:
+    """Bins per axis (x, y, z) of the bin grid for this geometry (cpmap_bin_grid)."""
     dims = (_i32 * 3)()
     _check("cpmap_bin_grid", library().cpmap_bin_grid(*_lat_args(lat), float(bin_size),
                                                        float(cutoff), dims))
@@ -241,6 +247,7 @@ def bin_grid(lat: Lattice, bin_size: float, cutoff: float) -> Tuple[int, int, in
 
 
 def workspace_layout(n_atoms: int, lat: Lattice, bin_size: float, cutoff: float):
+    """Byte offsets (bin_start, sorted atoms) inside a binned workspace."""
     a, b = _i64(), _i64()
     _check("cpmap_workspace_layout",
            library().cpmap_workspace_layout(int(n_atoms), *_lat_args(lat), float(bin_size),
@@ -296,6 +303,8 @@ def cutoff(workspace, n_atoms: int, lat: Lattice, bin_size: float, cutoff: float
 
 def slot_workspace_bytes(n_atoms: int, lat: Lattice, bin_size: float, cutoff: float,
                          capacity: int = 8) -> int:
+    """Bytes of the slot workspace bin_slots fills (cpmap_slot_workspace_bytes);
+    raises CpmapError for an invalid geometry or capacity."""
     n = library().cpmap_slot_workspace_bytes(int(n_atoms), *_lat_args(lat), float(bin_size),
                                              float(cutoff), int(capacity))
     if n == 0:
@@ -304,6 +313,7 @@ def slot_workspace_bytes(n_atoms: int, lat: Lattice, bin_size: float, cutoff: fl
 
 
 def slot_layout(n_atoms: int, lat: Lattice, bin_size: float, cutoff: float, capacity: int = 8):
+    """Byte offsets (slots, over_start, over_atoms) inside a slot workspace."""
     a, b, c = _i64(), _i64(), _i64()
     _check("cpmap_slot_layout",
            library().cpmap_slot_layout(int(n_atoms), *_lat_args(lat), float(bin_size),
