@@ -150,3 +150,22 @@ def test_oversized_axes_are_refused(big, axis):
     assert lib.cpmap_direct_workspace_bytes(1000, *d) == 0
     bd = (ctypes.c_int32 * 3)()
     assert lib.cpmap_bin_grid(*_lat(*d, 0.5, 0.0, 0.0, 0.0), 4.0, 12.0, bd) != OK
+
+
+@SETTINGS
+@given(n=st.sampled_from([2**31 - 2, 2**31 - 1, 2**31, 2**40, -1]), cap=st.integers(1, 256))
+def test_atom_count_limit_is_enforced(n, cap):
+    """n_atoms up to 2^31 - 1 is accepted by every size query and larger or
+    negative counts are refused (sizes 0, status EINVAL or ERANGE)."""
+    lib = cpmap.library()
+    L = _lat(64, 48, 40, 0.5, 0.0, 0.0, 0.0)
+    ok = 0 <= n <= 2**31 - 1
+    b = lib.cpmap_bin_workspace_bytes(n, *L, 4.0, 12.0)
+    sb = lib.cpmap_slot_workspace_bytes(n, *L, 4.0, 12.0, cap)
+    out = (ctypes.c_int32 * 5)()
+    st_plan = lib.cpmap_direct_plan(n, 64, 48, 40, 1, out)
+    if ok:
+        assert b >= 16 * n and sb >= 16 * n and st_plan == OK
+        assert 1 <= out[4] <= 32
+    else:
+        assert b == 0 and sb == 0 and st_plan != OK
