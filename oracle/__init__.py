@@ -11,7 +11,10 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# CPMAP_ORACLE_LIB points the loader at another build of cpmap_oracle.c: the
+# mutation test builds copies with planted mistakes and checks that the pins
+# fail on each.
+_LIB_PATH = os.environ.get("CPMAP_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 _f32p = np.ctypeslib.ndpointer(dtype=np.float32, flags="C_CONTIGUOUS")
