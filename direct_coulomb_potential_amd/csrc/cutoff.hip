@@ -257,15 +257,18 @@ __device__ __forceinline__ float term_at(float r2, const CutoffParams &P)
 // arithmetic, far below fp32 resolution.
 constexpr int kClampSearch = 64;
 
+// Every lane of the wave tests one candidate (lane k: k ulps below rc^2)
+// and the wave takes the first zero, so the search is one step.  Called with
+// the whole wave active.
 __device__ inline float exact_zero_clamp(const CutoffParams &P)
 {
-    uint32_t bits = __float_as_uint(P.rc2);
-    for (int k = 0; k < kClampSearch; ++k, --bits) {
-        const float r2 = __uint_as_float(bits);
-        if (term_at(r2, P) == 0.0f)
-            return r2;
-    }
-    return 0.0f;
+    static_assert(kClampSearch == 64, "one candidate per lane of a wave");
+    const uint32_t k = __lane_id();
+    const float r2 = __uint_as_float(__float_as_uint(P.rc2) - k);
+    const uint64_t zeros = __ballot(term_at(r2, P) == 0.0f);
+    if (zeros == 0)
+        return 0.0f;
+    return __uint_as_float(__float_as_uint(P.rc2) - (uint32_t)(__ffsll((long long)zeros) - 1));
 }
 
 // Charge-weighted moments of a set of atoms about a centre c, with a = atom -
