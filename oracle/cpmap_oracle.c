@@ -42,11 +42,13 @@
  *       last lattice node) + 1 + H.  Bins are linear x-fastest; atoms sorted
  *       stably by bin (input order inside a bin).
  *   R14 the hard-truncated cutoff (the notes' section 18.5 listing: q/r added
- *       only when r2 < rcut2) decides inclusion in fp32, exactly as the GPU
- *       kernel forms r2: dx, dy, dz = fl32(node - atom), r2 = fma(dx, dx,
- *       fma(dy, dy, fl32(dz*dz))), kept iff r2 < fl32(rc*rc).  The kept terms
- *       are summed in fp64.  (An inclusion decision is integer work, so both
- *       sides take it in the same precision.)
+ *       only when r2 < rcut2) decides inclusion with the listing's own fp32
+ *       expression: dx, dy, dz = fl32(node - atom), r2 = dx*dx + dy*dy + dz*dz
+ *       evaluated left to right, every product and sum rounded to fp32 (no
+ *       contraction: the build passes -ffp-contract=off), kept iff
+ *       r2 < rcut2 with rcut2 = fl32(rc*rc).  The kept terms are summed in
+ *       fp64.  (An inclusion decision is integer work decided in floating
+ *       point, so it is taken in the precision and order the page prints.)
  *   R15 ion placement (the notes' section 18.1: positive ions go where the
  *       potential is lowest, negative ions where it is highest): the extrema
  *       of V over its non-NaN nodes; among equal values the smallest node
@@ -210,20 +212,21 @@ void oracle_cutoff(const float *atoms, int64_t n_atoms,
     }
 }
 
-/* Inclusion test of the hard-truncated cutoff (reading R14), all fp32. */
+/* Inclusion test of the hard-truncated cutoff (reading R14): the section 18.5
+ * listing's r2 = dx*dx + dy*dy + dz*dz in fp32, left to right, no contraction. */
 static int hard_keep(float x, float y, float z, const float *a, float rc2f)
 {
     const float dx = x - a[0];
     const float dy = y - a[1];
     const float dz = z - a[2];
-    const float dz2 = dz * dz;
-    const float r2 = fmaf(dx, dx, fmaf(dy, dy, dz2));
+    const float r2 = dx * dx + dy * dy + dz * dz;
     return r2 < rc2f;
 }
 
 /*
  * Hard-truncated cutoff sum (the notes' section 18.5 listing; reading R14):
- * V = sum of q/r over the atoms the fp32 test keeps, r and the sum in fp64.
+ * V = sum of q/r over the atoms the listing's fp32 test keeps, r and the sum
+ * in fp64.
  * S receives sum |q|/r over the same atoms.
  */
 void oracle_cutoff_hard(const float *atoms, int64_t n_atoms,

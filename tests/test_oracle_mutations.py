@@ -59,7 +59,22 @@ MUTATIONS = [
     ("truncated: <= instead of <", "    return r2 < rc2f;", "    return r2 <= rc2f;"),
     ("truncated: decided in fp64", "    return r2 < rc2f;",
      "    return (double)dx * dx + (double)dy * dy + (double)dz * dz < (double)rc2f;"),
-    ("truncated: dz*dy for dz^2", "    const float dz2 = dz * dz;", "    const float dz2 = dz * dy;"),
+    ("truncated: dz*dy for dz^2", "const float r2 = dx * dx + dy * dy + dz * dz;",
+     "const float r2 = dx * dx + dy * dy + dz * dy;"),
+    ("truncated: fma chain instead of the listing's sum",
+     "const float r2 = dx * dx + dy * dy + dz * dz;",
+     "const float r2 = fmaf(dx, dx, fmaf(dy, dy, dz * dz));"),
+    ("truncated: listing's sum in reverse order",
+     "const float r2 = dx * dx + dy * dy + dz * dz;",
+     "const float r2 = dz * dz + dy * dy + dx * dx;"),
+    ("truncated: exact distance instead of fp32",
+     "    return r2 < rc2f;",
+     "    return (long double)dx * dx + (long double)dy * dy + (long double)dz * dz"
+     " < (long double)rc2f;"),
+    ("smoothed term: r^4 coefficient", "const double gamma = gc0 + r2 * (gc1 + r2 * gc2);",
+     "const double gamma = gc0 + r2 * (gc1 + r2 * gc2 * 1.0001);"),
+    ("smoothed term: gamma added, not subtracted", "return q * (1.0 / sqrt(r2) - gamma);",
+     "return q * (1.0 / sqrt(r2) + gamma);"),
 ]
 
 

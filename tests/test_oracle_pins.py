@@ -257,6 +257,60 @@ def test_cutoff_tends_to_direct_for_huge_cutoff():
         assert np.max(np.abs(Vc - Vd)) <= bound, rc
 
 
+def _dyadic_atoms(n, seed, lo=0.0, hi=4.0):
+    """n atoms at multiples of 1/8 in [lo, hi)^3 with charges k/16 in [-1, 1]:
+    every coordinate, difference, r^2 and charge is exact in fp32 and fp64."""
+    rng = np.random.default_rng(seed)
+    pos = rng.integers(int(lo * 8), int(hi * 8), size=(n, 3)) / 8.0
+    q = rng.integers(-16, 17, size=(n, 1)) / 16.0
+    return np.hstack([pos, q]).astype(np.float32)
+
+
+def _gamma_exact(r2, rc):
+    """gamma(r^2) = 15/(8 rc) - 5 r^2/(4 rc^3) + 3 r^4/(8 rc^5) (binning
+    lecture slide 24's GC0 + r2 (GC1 + r2 GC2), constants of the 100k-atom
+    cutoff workload) in exact rationals."""
+    rc = Fraction(rc)
+    return Fraction(15, 8) / rc - Fraction(5, 4) * r2 / rc**3 + Fraction(3, 8) * r2**2 / rc**5
+
+
+@pytest.mark.parametrize("rc", [16.0, 2.5])
+def test_cutoff_is_direct_minus_gamma_moments(rc):
+    """P7 as an identity: V_cut(g) = sum over r < rc of q/r minus sum over the
+    same atoms of q gamma(r^2).  On dyadic atoms and nodes r^2 is an exact
+    rational, so the kept set and sum q gamma are computed exactly here; the
+    q/r part is the direct oracle over the kept atoms.  rc = 16 exceeds every
+    distance (the whole direct sum); rc = 2.5 keeps part of the atoms (ties
+    r^2 = rc^2 are dropped, the strict test).  Agreement to fp64 rounding."""
+    A = _dyadic_atoms(60, seed=83)
+    dims, h, o = (3, 4, 3), 0.5, (0.25, 0.75, 1.25)
+    nodes = [(i, j, k) for k in range(dims[2]) for j in range(dims[1]) for i in range(dims[0])]
+    npos = [(o[0] + i * h, o[1] + j * h, o[2] + k * h) for i, j, k in nodes]
+    # no atom on a node
+    keep_atoms = [a for a in A if all(tuple(map(float, a[:3])) != p for p in npos)]
+    A = np.array(keep_atoms, dtype=np.float32)
+    Vc, Sc = oracle.cutoff(A, dims, h, o, rc, with_scale=True)
+    rc2 = Fraction(rc) ** 2
+    n_kept_total = 0
+    for t, p in enumerate(npos):
+        fr = [(sum((Fraction(float(a[d])) - Fraction(p[d])) ** 2 for d in range(3)), a)
+              for a in A]
+        kept = [(r2, a) for r2, a in fr if r2 < rc2]
+        n_kept_total += len(kept)
+        gam = sum(Fraction(float(a[3])) * _gamma_exact(r2, rc) for r2, a in kept)
+        sub = np.array([a for _, a in kept], dtype=np.float32).reshape(-1, 4)
+        Vd, Sd = oracle.direct(sub, (1, 1, 1), 1.0, p, with_scale=True)
+        want = Vd[0] - float(gam)
+        scale = Sd[0] + float(sum(abs(Fraction(float(a[3])) * _gamma_exact(r2, rc))
+                                  for r2, a in kept))
+        assert abs(Vc[t] - want) <= 64 * 2.0**-52 * scale, (t, Vc[t], want)
+        assert Sc[t] == pytest.approx(Sd[0], rel=1e-14, abs=0)
+    if rc > 10:
+        assert n_kept_total == len(A) * len(npos)
+    else:
+        assert 0 < n_kept_total < len(A) * len(npos)
+
+
 def test_cutoff_positive_charges_bounded_by_direct():
     """The term is >= 0 on (0, rc], so with q > 0: 0 <= V_cut <= V_direct."""
     A = random_atoms(300, (0, 0, 0), (20, 20, 20), seed=71, q_lo=0.0, q_hi=1.0)
@@ -412,19 +466,6 @@ def test_cutoff_hard_decision_is_taken_in_fp32():
     assert Vo[0] == 0.0
 
 
-# Atoms around a node at the origin, rc = 3, for which R14's fp32 chain and
-# the exact distance decide differently (found by a search in exact rational
-# arithmetic; the test re-derives the disagreement before relying on it).
-FP32_SPLIT_ATOMS = {
-    # exact r^2 = 9 - 1.4e-7 < 9, but the fp32 chain rounds r^2 to 9.0
-    "kept_exactly_dropped_in_fp32": (-0.1108543872833252, -1.9783434867858887,
-                                     2.2525248527526855),
-    # exact r^2 = 9 + 4.7e-8 >= 9, but the fp32 chain gives 8.999999
-    "dropped_exactly_kept_in_fp32": (-0.15722495317459106, 0.6464439630508423,
-                                     2.9253017902374268),
-}
-
-
 def _round_f32(fr):
     """The fp32 value nearest to the rational fr (ties to even)."""
     f = np.float32(float(fr))
@@ -433,32 +474,52 @@ def _round_f32(fr):
                                      int(np.array(c, np.float32).view(np.uint32)) & 1))
 
 
-def _fp32_chain_r2(dx, dy, dz):
-    """fma(dx, dx, fma(dy, dy, fl(dz*dz))), every step one rounding of its
-    exact value."""
-    def fr(v):
-        return Fraction(float(v))
-    dz2 = _round_f32(fr(dz) ** 2)
-    t = _round_f32(fr(dy) * fr(dy) + fr(dz2))
-    return _round_f32(fr(dx) * fr(dx) + fr(t))
+def _r2_forms(d):
+    """r^2 of the fp32 difference vector d formed four ways, each fp32 step
+    one correct rounding of its exact rational value: the section 18.5
+    listing (dx*dx + dy*dy) + dz*dz, the reversed sum, an fma chain
+    fma(dx, dx, fma(dy, dy, dz*dz)), and the exact value."""
+    fr = [Fraction(float(v)) for v in d]
+    sq = [_round_f32(v * v) for v in fr]
+    listing = _round_f32(Fraction(float(_round_f32(Fraction(float(sq[0])) +
+                                                   Fraction(float(sq[1]))))) +
+                         Fraction(float(sq[2])))
+    reverse = _round_f32(Fraction(float(_round_f32(Fraction(float(sq[2])) +
+                                                   Fraction(float(sq[1]))))) +
+                         Fraction(float(sq[0])))
+    fma = _round_f32(fr[0] * fr[0] + Fraction(float(_round_f32(fr[1] * fr[1] +
+                                                               Fraction(float(sq[2]))))))
+    return {"listing": Fraction(float(listing)), "reversed": Fraction(float(reverse)),
+            "fma": Fraction(float(fma)), "exact": sum(v * v for v in fr)}
 
 
-@pytest.mark.parametrize("case", sorted(FP32_SPLIT_ATOMS))
-def test_cutoff_hard_follows_fp32_where_the_exact_distance_disagrees(case):
-    """Reading R14 decides inclusion in fp32: an atom the exact distance
-    keeps but the fp32 chain rounds to rc^2 is dropped, and one the exact
-    distance drops but the fp32 chain puts below rc^2 is kept (V = q/r with
-    r within 1e-7 of rc)."""
-    a = np.array(FP32_SPLIT_ATOMS[case], dtype=np.float32)
+def _boundary_cases():
+    with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                           "truncated_boundary.json")) as f:
+        fx = json.load(f)
+    return [(c["kind"], c["atom"], fx["rc"]) for c in fx["cases"]]
+
+
+@pytest.mark.parametrize("kind,atom,rc", _boundary_cases(), ids=lambda v: str(v)[:28])
+def test_cutoff_hard_follows_the_listing_where_other_forms_disagree(kind, atom, rc):
+    """Reading R14: inclusion is the section 18.5 listing's fp32 test r2 =
+    dx*dx + dy*dy + dz*dz < rcut2, left to right.  Each fixture atom sits
+    within a few ulps of rc from a node at the origin, where the listing and
+    another form of r^2 (the exact distance, an fma chain, the reversed sum)
+    disagree; the disagreement is re-derived here in exact rational
+    arithmetic, and the oracle must keep the atom iff the listing does."""
+    a = np.array(atom, dtype=np.float32)
     d = -a  # node at the origin: node - atom, exact in fp32
-    kept_exact = sum(Fraction(float(v)) ** 2 for v in d) < 9
-    kept_fp32 = bool(_fp32_chain_r2(*d) < np.float32(9.0))
-    assert kept_fp32 != kept_exact
-    assert kept_fp32 == (case == "dropped_exactly_kept_in_fp32")
+    rc2 = Fraction(float(np.float32(rc) * np.float32(rc)))
+    assert rc2 == rc * rc
+    keep = {k: v < rc2 for k, v in _r2_forms(d).items()}
+    other = "exact" if kind.startswith("exact") else kind.split("_")[2]
+    assert keep["listing"] != keep[other], (kind, keep)
+    assert keep["listing"] == ("listing_keeps" in kind), (kind, keep)
     atoms = np.array([[*a, 0.75]], dtype=np.float32)
-    V, S = oracle.cutoff_hard(atoms, (1, 1, 1), 1.0, (0.0, 0.0, 0.0), 3.0, with_scale=True)
-    if kept_fp32:
-        assert V[0] == pytest.approx(0.25, rel=1e-7) and S[0] == pytest.approx(0.25, rel=1e-7)
+    V, S = oracle.cutoff_hard(atoms, (1, 1, 1), 1.0, (0.0, 0.0, 0.0), rc, with_scale=True)
+    if keep["listing"]:
+        assert V[0] == pytest.approx(0.25, rel=1e-6) and S[0] == pytest.approx(0.25, rel=1e-6)
     else:
         assert V[0] == 0.0 and S[0] == 0.0
 
