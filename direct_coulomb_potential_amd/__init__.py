@@ -68,8 +68,8 @@ _SIGNATURES = {
     "cpmap_cutoff_term": (_i32, [_vp, _sz, _i64, *_LAT, _f32, _f32, _i32, _vp, _vp]),
     "cpmap_extrema_workspace_bytes": (_sz, [_i64]),
     "cpmap_extrema": (_i32, [_vp, _i64, _vp, _vp, _vp, _sz, _vp]),
-    "cpmap_neighbor_spans": (_i64, [*_LAT, _f32, _f32, _i32, _i32, _i32, ctypes.POINTER(_i32),
-                                    _i64]),
+    "cpmap_neighbor_spans": (_i64, [*_LAT, _f32, _f32, _i32, _i32, _i32, _i32,
+                                    ctypes.POINTER(_i32), _i64]),
     "cpmap_slot_workspace_bytes": (_sz, [_i64, *_LAT, _f32, _f32, _i32]),
     "cpmap_slot_layout": (_i32, [_i64, *_LAT, _f32, _f32, _i32, ctypes.POINTER(_i64),
                                  ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
@@ -367,15 +367,19 @@ def cutoff_slots(slot_workspace, n_atoms: int, lat: Lattice, bin_size: float, cu
 
 
 def neighbor_spans(lat: Lattice, bin_size: float, cutoff: float, tile: Tuple[int, int, int],
-                   max_spans: int = 4096):
-    """x-runs of bins (cy, cz, cx_first, cx_last) the cutoff kernel walks for one tile."""
+                   max_spans: int = 4096, term: str = "smoothed"):
+    """x-runs of bins (cy, cz, cx_first, cx_last) the cutoff kernel walks for
+    one tile with this term."""
+    if term not in TERMS:
+        raise ValueError(f"term must be one of {sorted(TERMS)}")
     buf = (_i32 * (4 * max_spans))()
     n = library().cpmap_neighbor_spans(*_lat_args(lat), float(bin_size), float(cutoff),
-                                       int(tile[0]), int(tile[1]), int(tile[2]), buf, max_spans)
+                                       TERMS[term], int(tile[0]), int(tile[1]), int(tile[2]),
+                                       buf, max_spans)
     if n < 0:
         raise CpmapError("cpmap_neighbor_spans", 1, "invalid arguments")
     if n > max_spans:
-        return neighbor_spans(lat, bin_size, cutoff, tile, int(n))
+        return neighbor_spans(lat, bin_size, cutoff, tile, int(n), term)
     return [tuple(buf[4 * i:4 * i + 4]) for i in range(n)]
 
 

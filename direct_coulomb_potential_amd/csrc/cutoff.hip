@@ -5,8 +5,9 @@
 //              (the binning lecture's large-bin kernel slide gives the term;
 //              the constants make it vanish with two derivatives at rc);
 //   truncated  V(g) = sum q / r  (the case-study notes' section 18.5 listing),
-//              with the inclusion test taken in fp32 as r^2 = fma(dx, dx,
-//              fma(dy, dy, dz*dz)) < fl(rc*rc).
+//              with the listing's inclusion test: r2 = dx*dx + dy*dy + dz*dz
+//              in fp32, left to right, every step rounded (no fma), kept iff
+//              r2 < fl(rc*rc).
 //
 // Structure (the lecture's small-bin design, re-planned for CDNA4):
 //  - one workgroup per 8x8x8 tile of nodes (4 A of lattice at 0.5 A spacing,
@@ -201,7 +202,7 @@ struct CutoffParams {
     float b0[3];
     int32_t nb[3];
     float bs, rc, rc2;
-    float list_rc;  // radius of the bin neighbourhood (rc, widened for the truncated term)
+    float list_rc;  // radius of the bin neighbourhood (neighbourhood_radius)
     float gc0, gc1, gc2;
     int32_t truncated;
     int32_t cap;  // slots per bin (fixed-capacity source)
@@ -209,10 +210,24 @@ struct CutoffParams {
 
 constexpr int kWaves = kThreads / 64;
 
+// r2 as the case-study notes' section 18.5 listing forms it for its cutoff
+// test: dx*dx + dy*dy + dz*dz in fp32, left to right, every product and sum
+// rounded on its own.  Contraction into fused multiply-adds is switched off
+// here so that the inclusion decision is the listing's, bit for bit.
+__device__ __forceinline__ float listing_r2(float dx, float dy, float dz)
+{
+#pragma clang fp contract(off)
+    const float xx = dx * dx;
+    const float yy = dy * dy;
+    const float zz = dz * dz;
+    return (xx + yy) + zz;
+}
+
 // One staged atom against this lane's kNx nodes.  kSmoothClamp clamps r^2 to
 // P.rc2, for which the kernel has checked that the fp32 smoothed term is
 // exactly 0 (so atoms beyond the cutoff add exactly nothing); kSmoothSelect
-// and kTruncated replace the charge by 0 outside the cutoff.
+// and kTruncated replace the charge by 0 outside the cutoff, kTruncated with
+// the listing's r2.
 template <int MODE>
 __device__ __forceinline__ void add_atom(const float4 at, const float (&x)[kNx], float y, float z,
                                          const CutoffParams &P, float (&acc)[kNx])
@@ -237,7 +252,7 @@ __device__ __forceinline__ void add_atom(const float4 at, const float (&x)[kNx],
         } else if constexpr (MODE == kRsqInside) {
             acc[c] = fmaf(at.w, __builtin_amdgcn_rsqf(fmaf(dx, dx, yz2)), acc[c]);
         } else {
-            const float r2 = fmaf(dx, dx, yz2);
+            const float r2 = listing_r2(dx, dy, dz);
             const float qm = r2 < P.rc2 ? at.w : 0.0f;
             acc[c] = fmaf(qm, __builtin_amdgcn_rsqf(r2), acc[c]);
         }
@@ -702,6 +717,36 @@ cutoff_kernel(CutoffParams P0, const int32_t *__restrict__ bin_start,
 
 int32_t ceil_div32(int32_t a, int32_t b) { return (a + b - 1) / b; }
 
+// Radius of the bin neighbourhood a tile walks.  Two roundings can put an atom
+// outside its bin's box: its bin coordinate fl(fl(p - b0) / bs) is off by at
+// most 2^-23 |p - b0| per axis, and |p - b0| < nb bs for a kept atom, so the
+// box is widened by slack = 2^-21 max(nb bs) (>= sqrt(3) 2^-23 max(nb bs) with
+// room for the double geometry).  The truncated term's fp32 test can also
+// keep an atom whose exact distance exceeds rc by an ulp or two: a relative
+// 2^-16 covers that.  The smoothed term vanishes to third order at rc, so an
+// atom within `slack` of the cutoff adds at most 2.5 (slack/rc)^3 |q|/rc; the
+// slack is applied to it only where that bound could exceed 2^-30 |q|/rc
+// (slack > rc/1024, lattices some 10^4 cutoffs long), which keeps exact-tie
+// bins out of ordinary neighbourhoods.
+float neighbourhood_radius(const BinGeometry &g, int32_t term)
+{
+    double extent = 0.0;
+    for (int a = 0; a < 3; ++a)
+        extent = std::fmax(extent, (double)g.ax[a].nb * (double)g.bin_size);
+    const double rc = g.cutoff;
+    const double slack = std::ldexp(extent, -21);
+    double r = rc;
+    if (term == CPMAP_TERM_TRUNCATED)
+        r = rc * (1.0 + 1.0 / 65536.0) + slack;
+    else if (slack > rc / 1024.0)
+        r = rc + slack;
+    // round up so that the fp32 radius never falls below r
+    float f = (float)r;
+    if ((double)f < r)
+        f = std::nextafter(f, INFINITY);
+    return f;
+}
+
 
 CutoffParams make_params(const Lattice &lat, const BinGeometry &g, int32_t term, int32_t cap)
 {
@@ -719,11 +764,7 @@ CutoffParams make_params(const Lattice &lat, const BinGeometry &g, int32_t term,
     P.bs = g.bin_size;
     P.rc = g.cutoff;
     P.rc2 = g.cutoff * g.cutoff;
-    // The truncated term's fp32 inclusion test can keep an atom whose exact
-    // distance exceeds rc by an ulp, or whose bin rounding moved it across a
-    // face: widen its neighbourhood by a relative 2^-16 so that no kept atom
-    // is missed.  The smoothed term is ~1e-20 q there and needs no margin.
-    P.list_rc = P.truncated ? g.cutoff * (1.0f + 1.0f / 65536.0f) : g.cutoff;
+    P.list_rc = neighbourhood_radius(g, term);
     P.gc0 = (float)(15.0 / (8.0 * rc));
     P.gc1 = (float)(-5.0 / (4.0 * rc * rc * rc));
     P.gc2 = (float)(3.0 / (8.0 * rc * rc * rc * rc * rc));
@@ -783,12 +824,14 @@ hipError_t launch_cutoff_slots(const void *slot_workspace, const SlotLayout &S, 
 
 extern "C" int64_t cpmap_neighbor_spans(int32_t nx, int32_t ny, int32_t nz, float spacing,
                                         float ox, float oy, float oz, float bin_size,
-                                        float cutoff, int32_t tx, int32_t ty, int32_t tz,
-                                        int32_t *spans_out, int64_t max_spans)
+                                        float cutoff, int32_t term, int32_t tx, int32_t ty,
+                                        int32_t tz, int32_t *spans_out, int64_t max_spans)
 {
     using namespace cpmap;
     BinGeometry g;
     if (make_bin_geometry(nx, ny, nz, spacing, ox, oy, oz, bin_size, cutoff, &g) != CPMAP_OK)
+        return -1;
+    if (term != CPMAP_TERM_SMOOTHED && term != CPMAP_TERM_TRUNCATED)
         return -1;
     const int32_t n[3] = {nx, ny, nz};
     const int32_t t[3] = {tx, ty, tz};
@@ -800,7 +843,8 @@ extern "C" int64_t cpmap_neighbor_spans(int32_t nx, int32_t ny, int32_t nz, floa
     const float o[3] = {ox, oy, oz};
     const float b0[3] = {g.ax[0].b0, g.ax[1].b0, g.ax[2].b0};
     const int32_t nb[3] = {g.ax[0].nb, g.ax[1].nb, g.ax[2].nb};
-    const TileRows T = tile_rows(tx, ty, tz, n, spacing, o, b0, nb, bin_size, cutoff);
+    const TileRows T =
+        tile_rows(tx, ty, tz, n, spacing, o, b0, nb, bin_size, neighbourhood_radius(g, term));
     int64_t count = 0;
     for (int32_t r = 0; r < T.nrows; ++r) {
         int32_t cy, cz, cx0, cx1;

@@ -254,11 +254,13 @@ enum {
  * CPMAP_TERM_SMOOTHED is cpmap_cutoff.  CPMAP_TERM_TRUNCATED sums q / r over
  * the atoms with r^2 < rc^2 (the case-study notes' section 18.5 listing: the
  * bin scan adds q * rsqrt(r2) only when r2 < rcut2).  The inclusion test is
- * taken in fp32 exactly as r2 = fma(dx, dx, fma(dy, dy, dz*dz)) < fl(rc*rc),
- * with dx, dy, dz the fp32 differences node - atom, so that an atom at the
- * boundary is kept or dropped the same way on every call; the kept terms use
- * the hardware reciprocal square root.  The neighbourhood of bins is widened
- * by a relative 2^-16 for this term so that no kept atom is missed.
+ * the listing's, in fp32: dx, dy, dz = fl(node - atom) and
+ * r2 = dx*dx + dy*dy + dz*dz evaluated left to right with every product and
+ * sum rounded (no fused multiply-add), kept iff r2 < fl(rc*rc); so an atom at
+ * the boundary is kept or dropped as the listing decides it, on every call.
+ * The kept terms use the hardware reciprocal square root.  The neighbourhood
+ * of bins is widened for this term (cpmap_neighbor_spans) so that no kept
+ * atom is missed.
  *
  *   term   CPMAP_TERM_SMOOTHED or CPMAP_TERM_TRUNCATED (else CPMAP_EINVAL)
  * Other arguments, ownership and errors as cpmap_cutoff.
@@ -271,20 +273,28 @@ cpmap_status cpmap_cutoff_term(const void *workspace, size_t workspace_bytes, in
 
 /*
  * cpmap_neighbor_spans -- the neighbourhood the cutoff kernel walks for one
- * tile, for inspection and tests.  Host only, no HIP call.
+ * tile with one term, for inspection and tests.  Host only, no HIP call.
  *
  * The tile with tile coordinates (tx, ty, tz) holds nodes
  * [8tx, 8tx+8) x [8ty, 8ty+8) x [8tz, 8tz+8) clipped to the lattice.  A bin is
  * in its neighbourhood iff the distance between the tile's node bounding box
- * and the bin's box is < cutoff.  Such bins form runs along x; each run is
- * reported as (cy, cz, cx_first, cx_last) in spans_out (host, 4 int32 per
- * span, capacity max_spans).  Returns the number of spans (possibly larger
- * than max_spans, in which case only max_spans were written), or -1 on
- * invalid arguments.
+ * and the bin's box is < R (the binning lecture's neighbourhood offset list,
+ * with the box-to-box distance as the test), where R covers every atom the
+ * term can keep:
+ *   slack = 2^-21 * max over axes of (bins * bin_size)   (an atom's fp32 bin
+ *           coordinate can place it up to 2^-23 |p - b0| outside its bin);
+ *   CPMAP_TERM_SMOOTHED   R = cutoff, or cutoff + slack when slack exceeds
+ *                         cutoff / 1024 (the term vanishes to third order at
+ *                         the cutoff, so nearer misses add < 2^-30 |q|/rc);
+ *   CPMAP_TERM_TRUNCATED  R = cutoff * (1 + 2^-16) + slack.
+ * Such bins form runs along x; each run is reported as (cy, cz, cx_first,
+ * cx_last) in spans_out (host, 4 int32 per span, capacity max_spans).
+ * Returns the number of spans (possibly larger than max_spans, in which case
+ * only max_spans were written), or -1 on invalid arguments.
  */
 int64_t cpmap_neighbor_spans(int32_t nx, int32_t ny, int32_t nz, float spacing,
                              float ox, float oy, float oz,
-                             float bin_size, float cutoff,
+                             float bin_size, float cutoff, int32_t term,
                              int32_t tx, int32_t ty, int32_t tz,
                              int32_t *spans_out, int64_t max_spans);
 

@@ -70,7 +70,7 @@ int main()
             for (int32_t tx = -1; tx <= 3; ++tx)
                 for (int64_t cap : {0, 1, 64}) {
                     const int64_t k = cpmap_neighbor_spans(20, 17, 9, 0.5f, -2.0f, 1.0f, 0.25f, 1.5f,
-                                                           3.0f, tx, ty, tz,
+                                                           3.0f, (tx + ty) & 1, tx, ty, tz,
                                                            cap ? spans.data() : nullptr, cap);
                     const bool valid = tx >= 0 && ty >= 0 && tz >= 0 && tx < 3 && ty < 3 && tz < 2;
                     CHECK(valid ? k >= 0 : k == -1);

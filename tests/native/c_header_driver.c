@@ -27,9 +27,9 @@ int main(void)
     /* a lattice with a zero dimension is a documented no-op */
     CHECK(cpmap_direct(NULL, 0, 0, 4, 4, 0.5f, 0.f, 0.f, 0.f, NULL, NULL) == CPMAP_OK);
     CHECK(cpmap_direct(NULL, 0, 4, 4, 4, -0.5f, 0.f, 0.f, 0.f, NULL, NULL) == CPMAP_EINVAL);
-    n = cpmap_neighbor_spans(200, 200, 200, 0.5f, 0.f, 0.f, 0.f, 4.f, 12.f, 10, 10, 10, spans, 64);
+    n = cpmap_neighbor_spans(200, 200, 200, 0.5f, 0.f, 0.f, 0.f, 4.f, 12.f, CPMAP_TERM_SMOOTHED, 10, 10, 10, spans, 64);
     CHECK(n == 48);
-    CHECK(cpmap_neighbor_spans(200, 200, 200, 0.5f, 0.f, 0.f, 0.f, 4.f, 12.f, 25, 0, 0, spans, 64) == -1);
+    CHECK(cpmap_neighbor_spans(200, 200, 200, 0.5f, 0.f, 0.f, 0.f, 4.f, 12.f, CPMAP_TERM_SMOOTHED, 25, 0, 0, spans, 64) == -1);
     if (fails == 0)
         printf("ok\n");
     return fails != 0;

@@ -251,26 +251,75 @@ def test_truncated_boundary_decisions(torch):
     _parity(V, Vo, S, "truncated boundary")
 
 
-# Atoms around a node at the origin, rc = 3, for which the fp32 inclusion
-# chain and the exact distance disagree (the oracle pins re-derive this in
-# exact arithmetic): the first is dropped, the second kept.
-FP32_SPLIT_ATOMS = [((-0.1108543872833252, -1.9783434867858887, 2.2525248527526855), False),
-                    ((-0.15722495317459106, 0.6464439630508423, 2.9253017902374268), True)]
+def _boundary_atoms():
+    """Atoms within a few ulps of rc = 3 from a node at the origin on which the
+    case-study listing's fp32 r2 = dx*dx + dy*dy + dz*dz disagrees with the
+    exact distance, an fma chain or the reversed sum (tests/golden/
+    truncated_boundary.json; the oracle pins re-derive each disagreement in
+    exact arithmetic)."""
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                           "truncated_boundary.json")) as f:
+        fx = json.load(f)
+    return [(c["kind"], c["atom"]) for c in fx["cases"]]
 
 
-@pytest.mark.parametrize("atom,kept", FP32_SPLIT_ATOMS, ids=["dropped", "kept"])
+@pytest.mark.parametrize("kind,atom", _boundary_atoms(), ids=[k for k, _ in _boundary_atoms()])
 @pytest.mark.parametrize("bs", [1.0, 1.5, 4.0])
-def test_truncated_decision_matches_oracle_where_exact_distance_disagrees(torch, atom, kept, bs):
-    print(f"[truncated fp32 split] kept={kept} bs={bs}", flush=True)
+def test_truncated_decision_follows_the_listing(torch, kind, atom, bs):
+    print(f"[truncated listing decision] {kind} bs={bs}", flush=True)
     atoms_np = np.array([[*atom, 0.75]], dtype=np.float32)
     lat = Lattice(1, 1, 1, 1.0)
     ws = cpmap.bin_atoms(torch.from_numpy(atoms_np).cuda(), lat, bs, 3.0)
     V = cpmap.cutoff(ws, 1, lat, bs, 3.0, term="truncated").cpu().numpy().reshape(-1)
     Vo = oracle.cutoff_hard(atoms_np, lat.dims, lat.spacing, lat.origin, 3.0)
+    kept = "listing_keeps" in kind
     if kept:
         assert Vo[0] != 0.0 and abs(V[0] - Vo[0]) <= 1e-5 * abs(Vo[0])
     else:
         assert Vo[0] == 0.0 and V[0] == 0.0
+
+
+def _long_axis_case():
+    """Atoms at every fp32 value within 4 ulps of 60 bin faces near x = 1e6 A
+    on a 2^24-node axis (h = 1/16, bins of 1.3 A, rc = 1.505 A): some land,
+    by their fp32 bin coordinate, in a bin whose box they lie just outside of,
+    and a node within rc of them sits in a tile whose box is more than rc
+    from that bin (the host test of the neighbourhood counts these pairs)."""
+    nx, h, o, bs, rc = 1 << 24, 0.0625, 0.3, 1.3, 1.505
+    lat = Lattice(nx, 1, 1, h, (o, 0.0, 0.0))
+    _, b0, _ = oracle.bin_grid(lat.dims, h, lat.origin, bs, rc)
+    c0 = int((1e6 - float(b0[0])) / bs) - 60
+    rng = np.random.default_rng(23)
+    pts = []
+    for c in range(c0, c0 + 60):
+        f = np.float32(float(b0[0]) + c * bs)
+        vals = [f]
+        for _ in range(4):
+            vals = [np.nextafter(vals[0], np.float32(-np.inf))] + vals + \
+                   [np.nextafter(vals[-1], np.float32(np.inf))]
+        pts += [[float(v), float(np.float32(o)), 0.0, rng.uniform(-1, 1)] for v in vals]
+    atoms = np.array(pts, dtype=np.float32)
+    lo = int(np.floor((atoms[:, 0].min() - rc - np.float32(o)) / h)) - 8
+    hi = int(np.ceil((atoms[:, 0].max() + rc - np.float32(o)) / h)) + 8
+    near = np.arange(lo, hi, dtype=np.int64)
+    far = np.random.default_rng(24).integers(0, lo - 100, size=2000).astype(np.int64)
+    return lat, bs, rc, atoms, near, far
+
+
+@pytest.mark.parametrize("term", ["truncated", "smoothed"])
+def test_cutoff_long_axis_misbinned_atoms(torch, term):
+    print(f"[cutoff long axis] term={term}", flush=True)
+    lat, bs, rc, atoms_np, near, far = _long_axis_case()
+    atoms = torch.from_numpy(atoms_np).cuda()
+    ws = cpmap.bin_atoms(atoms, lat, bs, rc)
+    V = cpmap.cutoff(ws, atoms_np.shape[0], lat, bs, rc, term=term).cpu().numpy().reshape(-1)
+    fn = oracle.cutoff_hard if term == "truncated" else oracle.cutoff
+    Vo, S = fn(atoms_np, lat.dims, lat.spacing, lat.origin, rc, nodes=near, with_scale=True)
+    assert (S > 0).sum() > 1000
+    _parity(V[near], Vo, S, f"long axis {term}")
+    assert np.all(V[far] == 0.0)
 
 
 def test_truncated_config5_checked_nodes(torch):

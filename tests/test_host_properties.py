@@ -79,6 +79,7 @@ def test_bin_and_slot_layouts_are_consistent(nx, ny, nz, h, ox, oy, oz, bs, rc, 
        rc=cutoff, data=st.data())
 def test_neighbourhood_spans_stay_inside_the_bin_grid(nx, ny, nz, h, ox, oy, oz, bs, rc, data):
     lib = cpmap.library()
+    term = data.draw(st.sampled_from([0, 1]))
     L = _lat(nx, ny, nz, h, ox, oy, oz)
     bd = (ctypes.c_int32 * 3)()
     assume(lib.cpmap_bin_grid(*L, bs, rc, bd) == OK)
@@ -86,7 +87,7 @@ def test_neighbourhood_spans_stay_inside_the_bin_grid(nx, ny, nz, h, ox, oy, oz,
     t = [data.draw(st.integers(0, k - 1)) for k in tiles]
     cap = 4096
     buf = (ctypes.c_int32 * (4 * cap))()
-    count = lib.cpmap_neighbor_spans(*L, bs, rc, t[0], t[1], t[2], buf, cap)
+    count = lib.cpmap_neighbor_spans(*L, bs, rc, term, t[0], t[1], t[2], buf, cap)
     assert count >= 1  # the bins under the tile itself are always within rc
     rows = set()
     for i in range(min(count, cap)):
@@ -96,7 +97,7 @@ def test_neighbourhood_spans_stay_inside_the_bin_grid(nx, ny, nz, h, ox, oy, oz,
         assert (cy, cz) not in rows
         rows.add((cy, cz))
     # a tile outside the lattice is refused
-    assert lib.cpmap_neighbor_spans(*L, bs, rc, tiles[0], 0, 0, buf, cap) == -1
+    assert lib.cpmap_neighbor_spans(*L, bs, rc, term, tiles[0], 0, 0, buf, cap) == -1
 
 
 @SETTINGS

@@ -117,3 +117,65 @@ def test_spans_argument_errors():
         cpmap.neighbor_spans(lat, 4.0, 12.0, (2, 0, 0))
     with pytest.raises(cpmap.CpmapError):
         cpmap.neighbor_spans(lat, 0.0, 12.0, (0, 0, 0))
+
+
+def _fl32(x):
+    return float(np.float32(x))
+
+
+@pytest.mark.parametrize("term", ["smoothed", "truncated"])
+def test_spans_cover_atoms_misbinned_on_a_long_axis(term):
+    """On a long axis an atom's fp32 bin coordinate fl(fl(p - b0) / bs) can
+    put it in a bin whose box it lies just outside of.  Atoms at every fp32
+    value within a few ulps of bin faces near x = 1e6 A (h = 1/16, so a node
+    sits at every fp32 value there): every atom that a node keeps -- the exact
+    r < rc for the smoothed term, the case-study listing's fp32 r2 < rcut2
+    for the truncated one -- must sit, by the oracle's binning, in a bin of
+    that node's tile neighbourhood.  Some of these pairs fall outside a
+    neighbourhood of radius rc alone, so the check needs the slack."""
+    nx, h, o, bs, rc = 1 << 24, 0.0625, 0.3, 1.3, 1.505
+    lat = Lattice(nx, 1, 1, h, (o, 0.0, 0.0))
+    bins, b0, _ = oracle.bin_grid(lat.dims, h, lat.origin, bs, rc)
+    # 60 bin faces just below x = 1e6 and the fp32 values around each
+    atoms = []
+    c0 = int((1e6 - float(b0[0])) / bs) - 60
+    for c in range(c0, c0 + 60):
+        face = float(b0[0]) + c * bs
+        f = np.float32(face)
+        vals = [f]
+        for _ in range(4):
+            vals = [np.nextafter(vals[0], np.float32(-np.inf))] + vals + \
+                   [np.nextafter(vals[-1], np.float32(np.inf))]
+        atoms += [[float(v), _fl32(o), 0.0, 1.0] for v in vals]
+    atoms = np.array(atoms, dtype=np.float32)
+    _, _, bin_of = oracle.bin_atoms(atoms, lat.dims, h, lat.origin, bs, rc)
+    assert np.all(bin_of >= 0)
+    rc2_32 = np.float32(rc) * np.float32(rc)
+    spans_cache, missed_without_slack, checked = {}, 0, 0
+    for a, b in zip(atoms, bin_of):
+        p = float(a[0])
+        i_lo = int(np.floor((p - rc - _fl32(o)) / h)) - 1
+        for i in range(max(i_lo, 0), min(i_lo + int(2 * rc / h) + 4, nx)):
+            x = _fl32(_fl32(o) + i * h)  # one rounding of the exact o + i h
+            dx = np.float32(x) - a[0]  # exact: both near 1e6, Sterbenz
+            if term == "truncated":
+                kept = bool(np.float32(dx) * np.float32(dx) < rc2_32)
+            else:
+                kept = abs(x - p) < rc
+            if not kept:
+                continue
+            checked += 1
+            t = i // 8
+            if t not in spans_cache:
+                spans_cache[t] = cpmap.neighbor_spans(lat, bs, rc, (t, 0, 0), term=term)
+            cx, cy, cz = b % bins[0], (b // bins[0]) % bins[1], b // (bins[0] * bins[1])
+            assert any(sy == cy and sz == cz and s0 <= cx <= s1
+                       for sy, sz, s0, s1 in spans_cache[t]), (term, p, x, b)
+            # the same pair against a neighbourhood of radius rc alone
+            first, last = 8 * t, min(8 * t + 7, nx - 1)
+            xlo, xhi = _fl32(_fl32(o) + first * h), _fl32(_fl32(o) + last * h)
+            blo = float(b0[0]) + cx * bs
+            gap = max(0.0, blo - xhi, xlo - (blo + bs))
+            missed_without_slack += gap >= rc
+    assert checked > 1000
+    assert missed_without_slack > 0
