@@ -26,6 +26,7 @@ __all__ = [
     "bin_grid", "workspace_layout", "workspace_views", "neighbor_spans", "library",
     "library_path", "header_functions", "STATUS", "extrema", "place_ions", "TERMS",
     "slot_workspace_bytes", "slot_layout", "bin_slots", "slot_views", "cutoff_slots",
+    "node_position",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -75,6 +76,7 @@ _SIGNATURES = {
                                  ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
     "cpmap_bin_slots": (_i32, [_vp, _sz, _i64, *_LAT, _f32, _f32, _i32, _vp, _sz, _vp]),
     "cpmap_cutoff_slots": (_i32, [_vp, _sz, _i64, *_LAT, _f32, _f32, _i32, _i32, _vp, _vp]),
+    "cpmap_node_position": (_i32, [*_LAT, _i64, ctypes.POINTER(_i32), ctypes.POINTER(_f32)]),
 }
 
 
@@ -408,21 +410,22 @@ def extrema(V, workspace=None, out=None):
     return idx, val
 
 
+def node_position(lat: Lattice, index: int):
+    """((i, j, k), (x, y, z)) of the node a linear x-fastest index names
+    (cpmap_node_position: the position in the kernels' fp32 values)."""
+    ijk = (_i32 * 3)()
+    xyz = (_f32 * 3)()
+    _check("cpmap_node_position", library().cpmap_node_position(*_lat_args(lat), int(index),
+                                                                ijk, xyz))
+    return tuple(ijk), tuple(xyz)
+
+
 def place_ions(V, lat: Lattice):
     """Nodes for a positive ion (lowest potential) and a negative ion (highest),
-    as ((i, j, k), (x, y, z), value) pairs; synchronises to read them back."""
+    as ((i, j, k), (x, y, z), value) pairs, or None for a map with no non-NaN
+    node; synchronises to read the extrema back."""
     idx, val = extrema(V)
-    idx = idx.cpu().tolist()
-    val = val.cpu().tolist()
     out = []
-    for g, v in zip(idx, val):
-        if g < 0:
-            out.append(None)
-            continue
-        i, j, k = g % lat.nx, (g // lat.nx) % lat.ny, g // (lat.nx * lat.ny)
-        import numpy as np
-        h = float(np.float32(lat.spacing))
-        pos = tuple(float(np.float32(float(np.float32(o)) + c * h))  # one rounding, as the kernels
-                    for o, c in zip(lat.origin, (i, j, k)))
-        out.append(((i, j, k), pos, v))
+    for g, v in zip(idx.cpu().tolist(), val.cpu().tolist()):
+        out.append(None if g < 0 else (*node_position(lat, g), v))
     return {"positive_ion": out[0], "negative_ion": out[1]}

@@ -4,10 +4,9 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
-#include <mutex>
-#include <unordered_map>
 
 #include "cpmap_internal.h"
+#include "workspace_registry.h"
 
 namespace cpmap {
 
@@ -31,38 +30,18 @@ cpmap_status check_lattice(int32_t nx, int32_t ny, int32_t nz, float h, float ox
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Host-side record of the geometry each workspace was binned for (and the
-// slot capacity, for slot workspaces), so that the cutoff entry points can
-// reject a workspace filled for something else without reading device memory.
-struct WorkspaceKey {
-    int64_t n_atoms;
-    int32_t n[3];
-    float h, o[3], bs, rc;
-    int32_t cap;
-    bool operator==(const WorkspaceKey &k) const { return std::memcmp(this, &k, sizeof k) == 0; }
-};
-
-std::mutex g_mu;
-std::unordered_map<const void *, WorkspaceKey> g_binned;  // CSR workspaces
-std::unordered_map<const void *, WorkspaceKey> g_slotted; // slot workspaces
+// The workspaces the library has filled (see workspace_registry.h).
+WorkspaceRegistry g_registry;
 
 WorkspaceKey make_key(int64_t n_atoms, int32_t nx, int32_t ny, int32_t nz, float h, float ox,
                       float oy, float oz, float bs, float rc, int32_t cap = 0)
 {
-    WorkspaceKey k;
-    std::memset(&k, 0, sizeof k);  // padding bytes take part in operator==
-    k.n_atoms = n_atoms;
-    k.n[0] = nx;
-    k.n[1] = ny;
-    k.n[2] = nz;
-    k.h = h;
-    k.o[0] = ox;
-    k.o[1] = oy;
-    k.o[2] = oz;
-    k.bs = bs;
-    k.rc = rc;
-    k.cap = cap;
-    return k;
+    return WorkspaceKey::make(n_atoms, nx, ny, nz, h, ox, oy, oz, bs, rc, cap);
+}
+
+size_t map_bytes(int32_t nx, int32_t ny, int32_t nz)
+{
+    return sizeof(float) * (size_t)nx * (size_t)ny * (size_t)nz;
 }
 
 Lattice make_lattice(int32_t nx, int32_t ny, int32_t nz, float h, float ox, float oy, float oz)
@@ -206,9 +185,31 @@ cpmap_status cpmap_direct(const float *atoms, int64_t n_atoms, int32_t nx, int32
         return CPMAP_EINVAL;
     if (!aligned(V, 4) || (atoms && !aligned(atoms, 16)))
         return CPMAP_EINVAL;
+    g_registry.forget(V, map_bytes(nx, ny, nz));
     hipError_t e = launch_direct(reinterpret_cast<const float4 *>(atoms), n_atoms, lat, V,
                                  nullptr, 0, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? CPMAP_OK : CPMAP_EHIP;
+}
+
+cpmap_status cpmap_node_position(int32_t nx, int32_t ny, int32_t nz, float spacing, float ox,
+                                 float oy, float oz, int64_t index, int32_t *ijk_out,
+                                 float *xyz_out)
+{
+    if (ijk_out == nullptr || xyz_out == nullptr)
+        return CPMAP_EINVAL;
+    cpmap_status st = check_lattice(nx, ny, nz, spacing, ox, oy, oz);
+    if (st != CPMAP_OK)
+        return st;
+    const Lattice lat = make_lattice(nx, ny, nz, spacing, ox, oy, oz);
+    if (index < 0 || index >= lat.points())
+        return CPMAP_ERANGE;
+    const int64_t i = index % nx, j = (index / nx) % ny, k = index / ((int64_t)nx * ny);
+    const int64_t c[3] = {i, j, k};
+    for (int a = 0; a < 3; ++a) {
+        ijk_out[a] = (int32_t)c[a];
+        xyz_out[a] = node_coord(c[a], spacing, lat.o[a]);
+    }
+    return CPMAP_OK;
 }
 
 size_t cpmap_direct_workspace_bytes(int64_t n_atoms, int32_t nx, int32_t ny, int32_t nz)
@@ -244,6 +245,9 @@ cpmap_status cpmap_direct_with_workspace(const float *atoms, int64_t n_atoms, in
         return CPMAP_EINVAL;
     if (workspace_bytes < need)
         return CPMAP_ENOSPC;
+    g_registry.forget(V, map_bytes(nx, ny, nz));
+    if (need > 0)
+        g_registry.forget(workspace, need);
     hipError_t e = launch_direct(reinterpret_cast<const float4 *>(atoms), n_atoms, lat, V,
                                  need > 0 ? workspace : nullptr, workspace_bytes,
                                  static_cast<hipStream_t>(stream));
@@ -337,17 +341,15 @@ cpmap_status cpmap_bin_atoms(const float *atoms, int64_t n_atoms, int32_t nx, in
     if (workspace_bytes < L.total)
         return CPMAP_ENOSPC;
     const Lattice lat = make_lattice(nx, ny, nz, spacing, ox, oy, oz);
-    {
-        std::lock_guard<std::mutex> lock(g_mu);
-        g_binned.erase(workspace);
-        g_slotted.erase(workspace);
-    }
+    const uint64_t nonce =
+        g_registry.record(workspace, L.total, kBinnedWorkspace,
+                          make_key(n_atoms, nx, ny, nz, spacing, ox, oy, oz, bin_size, cutoff));
     hipError_t e = launch_bin_atoms(reinterpret_cast<const float4 *>(atoms), n_atoms, lat, g, L,
-                                    workspace, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess)
+                                    workspace, nonce, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+        g_registry.forget(workspace, L.total);
         return CPMAP_EHIP;
-    std::lock_guard<std::mutex> lock(g_mu);
-    g_binned[workspace] = make_key(n_atoms, nx, ny, nz, spacing, ox, oy, oz, bin_size, cutoff);
+    }
     return CPMAP_OK;
 }
 
@@ -373,15 +375,14 @@ cpmap_status cpmap_cutoff_term(const void *workspace, size_t workspace_bytes, in
     const BinLayout L = bin_layout(n_atoms, g);
     if (workspace_bytes < L.total)
         return CPMAP_ENOSPC;
-    {
-        std::lock_guard<std::mutex> lock(g_mu);
-        auto it = g_binned.find(workspace);
-        if (it == g_binned.end() ||
-            !(it->second == make_key(n_atoms, nx, ny, nz, spacing, ox, oy, oz, bin_size, cutoff)))
-            return CPMAP_EGEOM;
-    }
+    const uint64_t nonce =
+        g_registry.find(workspace, L.total, kBinnedWorkspace,
+                        make_key(n_atoms, nx, ny, nz, spacing, ox, oy, oz, bin_size, cutoff));
+    if (nonce == 0)
+        return CPMAP_EGEOM;
+    g_registry.forget(V, map_bytes(nx, ny, nz));
     const Lattice lat = make_lattice(nx, ny, nz, spacing, ox, oy, oz);
-    hipError_t e = launch_cutoff(workspace, L, n_atoms, lat, g, term, V,
+    hipError_t e = launch_cutoff(workspace, L, n_atoms, lat, g, term, nonce, V,
                                  static_cast<hipStream_t>(stream));
     return e == hipSuccess ? CPMAP_OK : CPMAP_EHIP;
 }
@@ -450,22 +451,20 @@ cpmap_status cpmap_bin_slots(const void *workspace, size_t workspace_bytes, int6
         return CPMAP_ENOSPC;
     if (overlaps(workspace, L.total, slot_workspace, S.total))
         return CPMAP_EINVAL;
-    {
-        std::lock_guard<std::mutex> lock(g_mu);
-        auto it = g_binned.find(workspace);
-        if (it == g_binned.end() ||
-            !(it->second == make_key(n_atoms, nx, ny, nz, spacing, ox, oy, oz, bin_size, cutoff)))
-            return CPMAP_EGEOM;
-        g_slotted.erase(slot_workspace);
-        g_binned.erase(slot_workspace);
-    }
-    hipError_t e = launch_bin_slots(workspace, L, n_atoms, g, capacity, slot_workspace, S,
-                                    static_cast<hipStream_t>(stream));
-    if (e != hipSuccess)
+    const uint64_t bin_nonce =
+        g_registry.find(workspace, L.total, kBinnedWorkspace,
+                        make_key(n_atoms, nx, ny, nz, spacing, ox, oy, oz, bin_size, cutoff));
+    if (bin_nonce == 0)
+        return CPMAP_EGEOM;
+    const uint64_t slot_nonce = g_registry.record(
+        slot_workspace, S.total, kSlotWorkspace,
+        make_key(n_atoms, nx, ny, nz, spacing, ox, oy, oz, bin_size, cutoff, capacity));
+    hipError_t e = launch_bin_slots(workspace, L, n_atoms, g, capacity, bin_nonce, slot_workspace,
+                                    S, slot_nonce, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+        g_registry.forget(slot_workspace, S.total);
         return CPMAP_EHIP;
-    std::lock_guard<std::mutex> lock(g_mu);
-    g_slotted[slot_workspace] =
-        make_key(n_atoms, nx, ny, nz, spacing, ox, oy, oz, bin_size, cutoff, capacity);
+    }
     return CPMAP_OK;
 }
 
@@ -489,17 +488,15 @@ cpmap_status cpmap_cutoff_slots(const void *slot_workspace, size_t slot_workspac
         return CPMAP_EINVAL;
     if (slot_workspace_bytes < S.total)
         return CPMAP_ENOSPC;
-    {
-        std::lock_guard<std::mutex> lock(g_mu);
-        auto it = g_slotted.find(slot_workspace);
-        if (it == g_slotted.end() ||
-            !(it->second ==
-              make_key(n_atoms, nx, ny, nz, spacing, ox, oy, oz, bin_size, cutoff, capacity)))
-            return CPMAP_EGEOM;
-    }
+    const uint64_t nonce = g_registry.find(
+        slot_workspace, S.total, kSlotWorkspace,
+        make_key(n_atoms, nx, ny, nz, spacing, ox, oy, oz, bin_size, cutoff, capacity));
+    if (nonce == 0)
+        return CPMAP_EGEOM;
+    g_registry.forget(V, map_bytes(nx, ny, nz));
     const Lattice lat = make_lattice(nx, ny, nz, spacing, ox, oy, oz);
-    hipError_t e = launch_cutoff_slots(slot_workspace, S, n_atoms, lat, g, capacity, term, V,
-                                       static_cast<hipStream_t>(stream));
+    hipError_t e = launch_cutoff_slots(slot_workspace, S, n_atoms, lat, g, capacity, term, nonce,
+                                       V, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? CPMAP_OK : CPMAP_EHIP;
 }
 
@@ -521,6 +518,7 @@ cpmap_status cpmap_direct_scatter(const float *atoms, int64_t n_atoms, int32_t n
         return CPMAP_EINVAL;
     if (!aligned(V, 4) || (atoms && !aligned(atoms, 16)))
         return CPMAP_EINVAL;
+    g_registry.forget(V, map_bytes(nx, ny, nz));
     hipError_t e = launch_scatter(reinterpret_cast<const float4 *>(atoms), n_atoms, lat, V,
                                   static_cast<hipStream_t>(stream));
     return e == hipSuccess ? CPMAP_OK : CPMAP_EHIP;
@@ -548,6 +546,9 @@ cpmap_status cpmap_extrema(const float *V, int64_t n, int64_t *out_index, float 
         return CPMAP_EINVAL;
     if (workspace_bytes < extrema_workspace_bytes(n))
         return CPMAP_ENOSPC;
+    g_registry.forget(out_index, 2 * sizeof(int64_t));
+    g_registry.forget(out_value, 2 * sizeof(float));
+    g_registry.forget(workspace, extrema_workspace_bytes(n));
     hipError_t e = launch_extrema(V, n, out_index, out_value, workspace,
                                   static_cast<hipStream_t>(stream));
     return e == hipSuccess ? CPMAP_OK : CPMAP_EHIP;

@@ -191,11 +191,15 @@ __global__ __launch_bounds__(kThreads) void k_scatter(
     }
 }
 
-// bin_start[b] = first position whose key >= b, for b in [0, nbins].
+// bin_start[b] = first position whose key >= b, for b in [0, nbins]; the
+// last kernel of a binning, so it also writes the workspace header.
 __global__ void k_starts(const int32_t *__restrict__ keys, int32_t n, int32_t nbins,
-                         int32_t *__restrict__ bin_start)
+                         int32_t *__restrict__ bin_start, WorkspaceHeader *__restrict__ hdr,
+                         WorkspaceHeader hdr_value)
 {
     const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (b == 0)
+        *hdr = hdr_value;
     if (b > nbins)
         return;
     int32_t lo = 0, hi = n;
@@ -236,8 +240,8 @@ BinLayout bin_layout(int64_t n_atoms, const BinGeometry &g)
     L.n_tiles = (n_atoms + kTileElems - 1) / kTileElems;
     L.passes = radix_passes(g.nbins());
     L.header = 0;
-    L.bin_start = 0;
-    L.sorted = up256(sizeof(int32_t) * (size_t)(g.nbins() + 1));
+    L.bin_start = kHeaderBytes;
+    L.sorted = up256(L.bin_start + sizeof(int32_t) * (size_t)(g.nbins() + 1));
     L.keys[0] = up256(L.sorted + 16 * n);
     L.keys[1] = up256(L.keys[0] + 4 * n);
     L.vals[0] = up256(L.keys[1] + 4 * n);
@@ -249,10 +253,12 @@ BinLayout bin_layout(int64_t n_atoms, const BinGeometry &g)
 
 hipError_t launch_bin_atoms(const float4 *atoms, int64_t n_atoms, const Lattice &lat,
                             const BinGeometry &g, const BinLayout &L, void *workspace,
-                            hipStream_t stream)
+                            uint64_t nonce, hipStream_t stream)
 {
     (void)lat;
     char *ws = static_cast<char *>(workspace);
+    WorkspaceHeader *hdr = reinterpret_cast<WorkspaceHeader *>(ws + L.header);
+    const WorkspaceHeader hv{kBinMagic, nonce};
     const int32_t n = (int32_t)n_atoms;
     const int32_t nbins = (int32_t)g.nbins();
     int32_t *bin_start = reinterpret_cast<int32_t *>(ws + L.bin_start);
@@ -292,10 +298,10 @@ hipError_t launch_bin_atoms(const float4 *atoms, int64_t n_atoms, const Lattice 
         hipLaunchKernelGGL(k_gather, dim3(grid_for(n)), dim3(kThreads), 0, stream, atoms,
                            vals[fin], n, sorted);
         hipLaunchKernelGGL(k_starts, dim3(grid_for((int64_t)nbins + 1)), dim3(kThreads), 0,
-                           stream, keys[fin], n, nbins, bin_start);
+                           stream, keys[fin], n, nbins, bin_start, hdr, hv);
     } else {
         hipLaunchKernelGGL(k_starts, dim3(grid_for((int64_t)nbins + 1)), dim3(kThreads), 0,
-                           stream, keys[0], 0, nbins, bin_start);
+                           stream, keys[0], 0, nbins, bin_start, hdr, hv);
     }
     return hipGetLastError();
 }

@@ -63,9 +63,22 @@ void direct_plan(int64_t n_atoms, const Lattice &lat, bool with_workspace, int32
 // Variants whose runtime occupancy differs from the planning table.
 int direct_occupancy_mismatches();
 
+// First bytes of a binned or slot workspace, written on the device by the
+// last kernel of the call that fills it and checked by every kernel that
+// reads it: `nonce` is the fill's number in the host registry (so a
+// workspace whose memory was reused and overwritten since, outside the
+// library, no longer matches its record).
+struct alignas(16) WorkspaceHeader {
+    uint64_t magic;
+    uint64_t nonce;
+};
+constexpr uint64_t kBinMagic = 0x4e49425f50414d43ull;   // "CMAP_BIN"
+constexpr uint64_t kSlotMagic = 0x544f4c535f50414dull;  // "MAP_SLOT"
+constexpr size_t kHeaderBytes = 256;
+
 // Workspace layout of the binned atoms.
 struct BinLayout {
-    size_t header;      // geometry header (bytes)
+    size_t header;      // WorkspaceHeader (kHeaderBytes reserved)
     size_t bin_start;   // offset of int32[nbins + 1]
     size_t sorted;      // offset of float4[n_atoms]
     size_t keys[2];     // int32[n_pad] radix-sort key ping-pong
@@ -78,17 +91,21 @@ struct BinLayout {
 
 BinLayout bin_layout(int64_t n_atoms, const BinGeometry &g);
 
+// Writes the header {kBinMagic, nonce} last.
 hipError_t launch_bin_atoms(const float4 *atoms, int64_t n_atoms, const Lattice &lat,
                             const BinGeometry &g, const BinLayout &L, void *workspace,
-                            hipStream_t stream);
+                            uint64_t nonce, hipStream_t stream);
 
+// Checks the header against {kBinMagic, nonce}; on a mismatch every node of V
+// is set to NaN and nothing else is read.
 hipError_t launch_cutoff(const void *workspace, const BinLayout &L, int64_t n_atoms,
-                         const Lattice &lat, const BinGeometry &g, int32_t term, float *V,
-                         hipStream_t stream);
+                         const Lattice &lat, const BinGeometry &g, int32_t term, uint64_t nonce,
+                         float *V, hipStream_t stream);
 
 // Fixed-capacity bins: cap slots per bin plus an overflow list in CSR form,
 // both derived from the stable CSR of a binned workspace.
 struct SlotLayout {
+    size_t header;      // WorkspaceHeader (kHeaderBytes reserved)
     size_t slots;       // float4[nbins * cap]
     size_t over_start;  // int32[nbins + 1]
     size_t over_atoms;  // float4[n_atoms]
@@ -99,14 +116,19 @@ struct SlotLayout {
 
 SlotLayout slot_layout(int64_t n_atoms, const BinGeometry &g, int32_t cap);
 
+// Reads a binned workspace whose header should be {kBinMagic, bin_nonce};
+// writes the slot header last: {kSlotMagic, slot_nonce}, or a nonce of 0
+// (which no record holds) when the binned header did not match.
 hipError_t launch_bin_slots(const void *bin_workspace, const BinLayout &L, int64_t n_atoms,
-                            const BinGeometry &g, int32_t cap, void *slot_workspace,
-                            const SlotLayout &S, hipStream_t stream);
+                            const BinGeometry &g, int32_t cap, uint64_t bin_nonce,
+                            void *slot_workspace, const SlotLayout &S, uint64_t slot_nonce,
+                            hipStream_t stream);
 
-// The slot pass, then the overflow pass adding into V.
+// The slot pass, then the overflow pass adding into V; both check the slot
+// header against {kSlotMagic, nonce} (NaN at every node on a mismatch).
 hipError_t launch_cutoff_slots(const void *slot_workspace, const SlotLayout &S, int64_t n_atoms,
                                const Lattice &lat, const BinGeometry &g, int32_t cap,
-                               int32_t term, float *V, hipStream_t stream);
+                               int32_t term, uint64_t nonce, float *V, hipStream_t stream);
 
 // Scatter form of the direct sum (atomics; a measured contrast).
 hipError_t launch_scatter(const float4 *atoms, int64_t n_atoms, const Lattice &lat, float *V,

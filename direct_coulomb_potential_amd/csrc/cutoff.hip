@@ -206,6 +206,7 @@ struct CutoffParams {
     float gc0, gc1, gc2;
     int32_t truncated;
     int32_t cap;  // slots per bin (fixed-capacity source)
+    uint64_t magic, nonce;  // the workspace header the atoms' record expects
 };
 
 constexpr int kWaves = kThreads / 64;
@@ -410,10 +411,39 @@ __device__ __forceinline__ void sweep(const float4 *stage, const uint32_t *list,
 // SLOTS = false: the atoms are a CSR (bin_start, sorted); SLOTS = true: they
 // are fixed-capacity bins, bin b's slots at sorted[b * cap ...], and
 // bin_start is not read.  ACCUM = true adds the sum into V.
+// Store of this thread's kNx nodes of the tile (x-fastest rows of V); the
+// indices are recomputed here rather than kept through the sweep (the empty
+// asm keeps the compiler from reusing the early ones).
+template <bool ACCUM>
+__device__ __forceinline__ void store_nodes(const CutoffParams &P, int32_t tx, int32_t ty,
+                                            int32_t tz, const float (&v)[kNx],
+                                            float *__restrict__ V)
+{
+    int32_t te = threadIdx.x;
+    asm volatile("" : "+v"(te));
+    const int32_t qs = (te % 64) / kGroupLanes, ls = te % kGroupLanes;
+    const int32_t i0s = tx * kTile + (qs & 1) * kCube;
+    const int32_t js = ty * kTile + (qs >> 1) * kCube + ls % kCube;
+    const int32_t ks = tz * kTile + (te / 64) * kCube + ls / kCube;
+    if (js >= P.n[1] || ks >= P.n[2])
+        return;
+    float *out = V + ((int64_t)ks * P.n[1] + js) * P.n[0];
+#pragma unroll
+    for (int c = 0; c < kNx; ++c) {
+        if (i0s + c < P.n[0]) {
+            if constexpr (ACCUM)
+                out[i0s + c] += v[c];
+            else
+                out[i0s + c] = v[c];
+        }
+    }
+}
+
 template <bool SLOTS, bool ACCUM>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd))) void
-cutoff_kernel(CutoffParams P0, const int32_t *__restrict__ bin_start,
-              const float4 *__restrict__ sorted, int32_t n_sorted, float *__restrict__ V)
+cutoff_kernel(CutoffParams P0, const WorkspaceHeader *__restrict__ hdr,
+              const int32_t *__restrict__ bin_start, const float4 *__restrict__ sorted,
+              int32_t n_sorted, float *__restrict__ V)
 {
     __shared__ float4 stage[kStage];
     __shared__ uint32_t cube_list[kWaves][kGroups][kStage];  // byte offsets into stage
@@ -440,6 +470,15 @@ cutoff_kernel(CutoffParams P0, const int32_t *__restrict__ bin_start,
     const int32_t tx = tile % P.tiles[0];
     const int32_t ty = (tile / P.tiles[0]) % P.tiles[1];
     const int32_t tz = tile / (P.tiles[0] * P.tiles[1]);
+    // A workspace whose header no longer carries the fill its record names
+    // (its memory was reused and overwritten since) is not read: every node
+    // becomes NaN.
+    if (hdr->magic != P0.magic || hdr->nonce != P0.nonce) {
+        const float nan = __builtin_nanf("");
+        const float v[kNx] = {nan, nan, nan, nan};
+        store_nodes<false>(P0, tx, ty, tz, v, V);
+        return;
+    }
     // The tile's geometry is the same for every thread: computed once and
     // kept in LDS, so its doubles do not occupy registers through the sweep.
     __shared__ TileRows T;
@@ -688,31 +727,14 @@ cutoff_kernel(CutoffParams P0, const int32_t *__restrict__ bin_start,
             acc_in[c] -= moments_poly(mom, x[c] - centre[0], y - centre[1], z - centre[2], P);
     }
 
-    // The store's indices again: cheaper to recompute than to keep through
-    // the sweep (the empty asm keeps the compiler from reusing the early ones).
-    int32_t te = threadIdx.x;
-    asm volatile("" : "+v"(te));
-    const int32_t qs = (te % 64) / kGroupLanes, ls = te % kGroupLanes;
-    const int32_t i0s = tx * kTile + (qs & 1) * kCube;
-    const int32_t js = ty * kTile + (qs >> 1) * kCube + ls % kCube;
-    const int32_t ks = tz * kTile + (te / 64) * kCube + ls / kCube;
-    if (js >= P.n[1] || ks >= P.n[2])
-        return;
-    float *out = V + ((int64_t)ks * P.n[1] + js) * P.n[0];
-    if constexpr (ACCUM) {
-        // nothing within reach of this tile: its nodes keep their value
-        if (!any_atoms)
-            return;
-#pragma unroll
-        for (int c = 0; c < kNx; ++c)
-            if (i0s + c < P.n[0])
-                out[i0s + c] += acc_in[c] + acc_bd[c];
-        return;
-    }
+    float v[kNx];
 #pragma unroll
     for (int c = 0; c < kNx; ++c)
-        if (i0s + c < P.n[0])
-            out[i0s + c] = acc_in[c] + acc_bd[c];
+        v[c] = acc_in[c] + acc_bd[c];
+    // overflow pass: nothing within reach of this tile, its nodes keep their value
+    if (ACCUM && !any_atoms)
+        return;
+    store_nodes<ACCUM>(P, tx, ty, tz, v, V);
 }
 
 int32_t ceil_div32(int32_t a, int32_t b) { return (a + b - 1) / b; }
@@ -748,9 +770,12 @@ float neighbourhood_radius(const BinGeometry &g, int32_t term)
 }
 
 
-CutoffParams make_params(const Lattice &lat, const BinGeometry &g, int32_t term, int32_t cap)
+CutoffParams make_params(const Lattice &lat, const BinGeometry &g, int32_t term, int32_t cap,
+                         uint64_t magic, uint64_t nonce)
 {
     CutoffParams P;
+    P.magic = magic;
+    P.nonce = nonce;
     P.truncated = term == CPMAP_TERM_TRUNCATED;
     P.h = lat.h;
     for (int a = 0; a < 3; ++a) {
@@ -780,43 +805,45 @@ int64_t tile_count(const CutoffParams &P)
 }  // namespace
 
 hipError_t launch_cutoff(const void *workspace, const BinLayout &L, int64_t n_atoms,
-                         const Lattice &lat, const BinGeometry &g, int32_t term, float *V,
-                         hipStream_t stream)
+                         const Lattice &lat, const BinGeometry &g, int32_t term, uint64_t nonce,
+                         float *V, hipStream_t stream)
 {
-    const CutoffParams P = make_params(lat, g, term, 0);
+    const CutoffParams P = make_params(lat, g, term, 0, kBinMagic, nonce);
     const int64_t tiles = tile_count(P);
     if (tiles == 0)
         return hipSuccess;
     if (tiles > INT32_MAX)
         return hipErrorInvalidValue;
     const char *ws = static_cast<const char *>(workspace);
+    const WorkspaceHeader *hdr = reinterpret_cast<const WorkspaceHeader *>(ws + L.header);
     const int32_t *bin_start = reinterpret_cast<const int32_t *>(ws + L.bin_start);
     const float4 *sorted = reinterpret_cast<const float4 *>(ws + L.sorted);
     hipLaunchKernelGGL((cutoff_kernel<false, false>), dim3((unsigned)tiles), dim3(kThreads), 0,
-                       stream, P, bin_start, sorted, (int32_t)n_atoms, V);
+                       stream, P, hdr, bin_start, sorted, (int32_t)n_atoms, V);
     return hipGetLastError();
 }
 
 hipError_t launch_cutoff_slots(const void *slot_workspace, const SlotLayout &S, int64_t n_atoms,
                                const Lattice &lat, const BinGeometry &g, int32_t cap,
-                               int32_t term, float *V, hipStream_t stream)
+                               int32_t term, uint64_t nonce, float *V, hipStream_t stream)
 {
-    const CutoffParams Pslots = make_params(lat, g, term, cap);
-    const CutoffParams Pover = make_params(lat, g, term, 0);
+    const CutoffParams Pslots = make_params(lat, g, term, cap, kSlotMagic, nonce);
+    const CutoffParams Pover = make_params(lat, g, term, 0, kSlotMagic, nonce);
     const int64_t tiles = tile_count(Pslots);
     if (tiles == 0)
         return hipSuccess;
     if (tiles > INT32_MAX)
         return hipErrorInvalidValue;
     const char *ws = static_cast<const char *>(slot_workspace);
+    const WorkspaceHeader *hdr = reinterpret_cast<const WorkspaceHeader *>(ws + S.header);
     const float4 *slots = reinterpret_cast<const float4 *>(ws + S.slots);
     const int32_t *over_start = reinterpret_cast<const int32_t *>(ws + S.over_start);
     const float4 *over_atoms = reinterpret_cast<const float4 *>(ws + S.over_atoms);
     const int64_t n_slots = g.nbins() * cap;
     hipLaunchKernelGGL((cutoff_kernel<true, false>), dim3((unsigned)tiles), dim3(kThreads), 0,
-                       stream, Pslots, nullptr, slots, (int32_t)n_slots, V);
+                       stream, Pslots, hdr, nullptr, slots, (int32_t)n_slots, V);
     hipLaunchKernelGGL((cutoff_kernel<false, true>), dim3((unsigned)tiles), dim3(kThreads), 0,
-                       stream, Pover, over_start, over_atoms, (int32_t)n_atoms, V);
+                       stream, Pover, hdr, over_start, over_atoms, (int32_t)n_atoms, V);
     return hipGetLastError();
 }
 

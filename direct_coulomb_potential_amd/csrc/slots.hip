@@ -35,25 +35,39 @@ unsigned blocks_for(int64_t n, int64_t cap_blocks)
     return (unsigned)(b < 1 ? 1 : b);
 }
 
-__device__ __forceinline__ int32_t over_count(const int32_t *__restrict__ bin_start, int64_t b,
-                                              int32_t cap)
+// Atoms of bin b: [*start, *start + count), with the CSR offsets clamped to
+// [0, n] so that a workspace whose contents changed since it was binned can
+// give wrong slots but never an access outside the sorted atoms.
+__device__ __forceinline__ int32_t bin_range(const int32_t *__restrict__ bin_start, int64_t b,
+                                             int32_t n, int32_t *start)
 {
-    const int32_t c = bin_start[b + 1] - bin_start[b] - cap;
+    int32_t s = bin_start[b], e = bin_start[b + 1];
+    s = s < 0 ? 0 : (s > n ? n : s);
+    e = e < s ? s : (e > n ? n : e);
+    *start = s;
+    return e - s;
+}
+
+__device__ __forceinline__ int32_t over_count(const int32_t *__restrict__ bin_start, int64_t b,
+                                              int32_t n, int32_t cap)
+{
+    int32_t s;
+    const int32_t c = bin_range(bin_start, b, n, &s) - cap;
     return c > 0 ? c : 0;
 }
 
 __global__ __launch_bounds__(kThreads) void slot_fill(const int32_t *__restrict__ bin_start,
                                                       const float4 *__restrict__ sorted,
-                                                      int64_t n_slots, int32_t cap,
-                                                      float4 *__restrict__ slots)
+                                                      int32_t n_atoms, int64_t n_slots,
+                                                      int32_t cap, float4 *__restrict__ slots)
 {
     const float inf = __builtin_huge_valf();
     const int64_t stride = (int64_t)gridDim.x * kThreads;
     for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < n_slots; e += stride) {
         const int64_t b = e / cap;
         const int32_t s = (int32_t)(e - b * cap);
-        const int32_t start = bin_start[b];
-        const int32_t count = bin_start[b + 1] - start;
+        int32_t start;
+        const int32_t count = bin_range(bin_start, b, n_atoms, &start);
         slots[e] = s < count ? sorted[start + s] : make_float4(inf, inf, inf, 0.0f);
     }
 }
@@ -79,14 +93,15 @@ __device__ int32_t block_exclusive_scan(int32_t v, int32_t *total)
 }
 
 __global__ __launch_bounds__(kThreads) void over_chunk_sums(const int32_t *__restrict__ bin_start,
-                                                            int64_t nbins, int32_t cap,
+                                                            int32_t n_atoms, int64_t nbins,
+                                                            int32_t cap,
                                                             int32_t *__restrict__ chunk_sum)
 {
     const int64_t first = (int64_t)blockIdx.x * kChunkBins + threadIdx.x * kBinsPerThread;
     int32_t local = 0;
     for (int i = 0; i < kBinsPerThread; ++i)
         if (first + i < nbins)
-            local += over_count(bin_start, first + i, cap);
+            local += over_count(bin_start, first + i, n_atoms, cap);
     int32_t total;
     block_exclusive_scan(local, &total);
     if (threadIdx.x == 0)
@@ -112,7 +127,8 @@ __global__ __launch_bounds__(kThreads) void over_chunk_scan(int32_t *__restrict_
 }
 
 __global__ __launch_bounds__(kThreads) void over_starts(const int32_t *__restrict__ bin_start,
-                                                        int64_t nbins, int32_t cap,
+                                                        int32_t n_atoms, int64_t nbins,
+                                                        int32_t cap,
                                                         const int32_t *__restrict__ chunk_sum,
                                                         int64_t n_chunks,
                                                         int32_t *__restrict__ over_start)
@@ -121,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void over_starts(const int32_t *__restric
     int32_t c[kBinsPerThread];
     int32_t local = 0;
     for (int i = 0; i < kBinsPerThread; ++i) {
-        c[i] = first + i < nbins ? over_count(bin_start, first + i, cap) : 0;
+        c[i] = first + i < nbins ? over_count(bin_start, first + i, n_atoms, cap) : 0;
         local += c[i];
     }
     int32_t total;
@@ -136,7 +152,9 @@ __global__ __launch_bounds__(kThreads) void over_starts(const int32_t *__restric
 }
 
 // keys[p] is the bin of sorted atom p (the radix sort's final keys; dropped
-// atoms carry nbins and sort last).
+// atoms carry nbins and sort last).  Destinations outside [0, n_atoms) --
+// possible only when the binned workspace changed since it was binned --
+// are skipped.
 __global__ __launch_bounds__(kThreads) void over_place(const int32_t *__restrict__ keys,
                                                        const int32_t *__restrict__ bin_start,
                                                        const float4 *__restrict__ sorted,
@@ -151,9 +169,23 @@ __global__ __launch_bounds__(kThreads) void over_place(const int32_t *__restrict
         if (b < 0 || b >= nbins)
             continue;
         const int64_t rank = p - bin_start[b];
-        if (rank >= cap)
-            over_atoms[over_start[b] + (rank - cap)] = sorted[p];
+        if (rank >= cap) {
+            const int64_t dst = (int64_t)over_start[b] + (rank - cap);
+            if (dst >= 0 && dst < n_atoms)
+                over_atoms[dst] = sorted[p];
+        }
     }
+}
+
+// The slot workspace's header, written last: the slot fill's number if the
+// binned workspace it read still carried the header its record expects,
+// else 0, which no record holds (the cutoff kernels then refuse the slots).
+__global__ void slot_header(const WorkspaceHeader *__restrict__ bin_hdr, uint64_t bin_nonce,
+                            uint64_t slot_nonce, WorkspaceHeader *__restrict__ hdr)
+{
+    const bool ok = bin_hdr->magic == kBinMagic && bin_hdr->nonce == bin_nonce;
+    hdr->magic = kSlotMagic;
+    hdr->nonce = ok ? slot_nonce : 0;
 }
 
 }  // namespace
@@ -163,7 +195,8 @@ SlotLayout slot_layout(int64_t n_atoms, const BinGeometry &g, int32_t cap)
     SlotLayout S{};
     const size_t nbins = (size_t)g.nbins();
     S.n_chunks = ((int64_t)nbins + kChunkBins - 1) / kChunkBins;
-    S.slots = 0;
+    S.header = 0;
+    S.slots = kHeaderBytes;
     S.over_start = up256(S.slots + sizeof(float4) * nbins * (size_t)cap);
     S.over_atoms = up256(S.over_start + sizeof(int32_t) * (nbins + 1));
     S.chunk_sum = up256(S.over_atoms + sizeof(float4) * (size_t)n_atoms);
@@ -172,11 +205,15 @@ SlotLayout slot_layout(int64_t n_atoms, const BinGeometry &g, int32_t cap)
 }
 
 hipError_t launch_bin_slots(const void *bin_workspace, const BinLayout &L, int64_t n_atoms,
-                            const BinGeometry &g, int32_t cap, void *slot_workspace,
-                            const SlotLayout &S, hipStream_t stream)
+                            const BinGeometry &g, int32_t cap, uint64_t bin_nonce,
+                            void *slot_workspace, const SlotLayout &S, uint64_t slot_nonce,
+                            hipStream_t stream)
 {
     const char *bw = static_cast<const char *>(bin_workspace);
     char *sw = static_cast<char *>(slot_workspace);
+    const WorkspaceHeader *bin_hdr = reinterpret_cast<const WorkspaceHeader *>(bw + L.header);
+    WorkspaceHeader *hdr = reinterpret_cast<WorkspaceHeader *>(sw + S.header);
+    const int32_t n = (int32_t)n_atoms;
     const int32_t *bin_start = reinterpret_cast<const int32_t *>(bw + L.bin_start);
     const float4 *sorted = reinterpret_cast<const float4 *>(bw + L.sorted);
     const int32_t *keys = reinterpret_cast<const int32_t *>(bw + L.keys[L.passes & 1]);
@@ -188,17 +225,19 @@ hipError_t launch_bin_slots(const void *bin_workspace, const BinLayout &L, int64
     const int64_t n_slots = nbins * cap;
 
     hipLaunchKernelGGL(slot_fill, dim3(blocks_for(n_slots, 8192)), dim3(kThreads), 0, stream,
-                       bin_start, sorted, n_slots, cap, slots);
+                       bin_start, sorted, n, n_slots, cap, slots);
     hipLaunchKernelGGL(over_chunk_sums, dim3((unsigned)S.n_chunks), dim3(kThreads), 0, stream,
-                       bin_start, nbins, cap, chunk_sum);
+                       bin_start, n, nbins, cap, chunk_sum);
     hipLaunchKernelGGL(over_chunk_scan, dim3(1), dim3(kThreads), 0, stream, chunk_sum,
                        S.n_chunks);
     hipLaunchKernelGGL(over_starts, dim3((unsigned)S.n_chunks), dim3(kThreads), 0, stream,
-                       bin_start, nbins, cap, chunk_sum, S.n_chunks, over_start);
+                       bin_start, n, nbins, cap, chunk_sum, S.n_chunks, over_start);
     if (n_atoms > 0)
         hipLaunchKernelGGL(over_place, dim3(blocks_for(n_atoms, 8192)), dim3(kThreads), 0,
                            stream, keys, bin_start, sorted, n_atoms, nbins, cap, over_start,
                            over_atoms);
+    hipLaunchKernelGGL(slot_header, dim3(1), dim3(1), 0, stream, bin_hdr, bin_nonce, slot_nonce,
+                       hdr);
     return hipGetLastError();
 }
 

@@ -44,7 +44,8 @@ typedef enum cpmap_status {
     CPMAP_ERANGE = 2, /* a count or index does not fit the library's limits */
     CPMAP_ENOSPC = 3, /* workspace smaller than cpmap_bin_workspace_bytes() */
     CPMAP_EGEOM = 4,  /* workspace was binned for another geometry or atom
-                         count, or was never binned */
+                         count, was never binned, or was written since (see
+                         "Workspace records" below) */
     CPMAP_EHIP = 5    /* the HIP runtime reported an error at launch */
 } cpmap_status;
 
@@ -59,6 +60,24 @@ const char *cpmap_status_str(int32_t status);
 #define CPMAP_MAX_ATOMS 2147483647LL
 #define CPMAP_MAX_DIM 16777216
 #define CPMAP_MAX_POINTS 68719476736LL
+
+/*
+ * cpmap_node_position -- the node a linear index of a lattice map names, and
+ * its position.  Host only, no HIP call.
+ *
+ * For index = (k*ny + j)*nx + i (the x-fastest order of V, the notes' section
+ * 18.4) writes ijk_out (host, 3 int32) = (i, j, k) and xyz_out (host, 3
+ * floats) = the node's position (fl(ox + i*spacing), fl(oy + j*spacing),
+ * fl(oz + k*spacing)), the same fp32 values the kernels use (the gather
+ * listing of section 18.2 puts node (gx, gy, gz) at (gx, gy, gz)*h).  With
+ * cpmap_extrema it places ions at nodes (section 18.1: positive ions where
+ * the potential is lowest, negative ions where it is highest).
+ * Returns CPMAP_EINVAL for a null output or an invalid lattice, CPMAP_ERANGE
+ * when index is outside [0, nx*ny*nz).
+ */
+cpmap_status cpmap_node_position(int32_t nx, int32_t ny, int32_t nz, float spacing,
+                                 float ox, float oy, float oz, int64_t index,
+                                 int32_t *ijk_out, float *xyz_out);
 
 /*
  * cpmap_direct -- direct Coulomb summation over every atom.
@@ -161,6 +180,28 @@ int32_t cpmap_direct_occupancy_check(void);
  */
 
 /*
+ * Workspace records.  cpmap_bin_atoms and cpmap_bin_slots record, on the host,
+ * the range they fill, what they filled it for (atom count, lattice, bin size,
+ * cutoff, capacity) and a fill number, and write a 16-byte header with that
+ * number at the workspace's start (byte offset 0; the layouts below leave
+ * its first 256 bytes to it).  A call that reads a filled workspace
+ * (cpmap_cutoff, cpmap_cutoff_term, cpmap_bin_slots, cpmap_cutoff_slots)
+ * returns CPMAP_EGEOM unless a record with the same base address, size and
+ * arguments exists.  Every call that writes device memory (any V, any
+ * workspace, the extrema outputs) first drops the records of the ranges it
+ * writes, so a workspace rebinned through another address or used as an
+ * output or scratch buffer by this library is refused afterwards.  Memory
+ * written outside the library (for instance freed and reused by another
+ * tensor) cannot be seen on the host: the cutoff kernels then compare the
+ * device header with the record and, on a mismatch, read nothing and set
+ * every node of V to NaN (cpmap_bin_slots passes the mismatch on to the slot
+ * workspace).  A change that leaves the header intact but alters the bins
+ * is not detected: the kernels clamp every offset they read, so it can give a
+ * wrong map but never an access outside the workspace.  Records are kept
+ * per process; calls from several threads are safe.
+ */
+
+/*
  * cpmap_bin_workspace_bytes -- size of the workspace that cpmap_bin_atoms
  * fills and cpmap_cutoff reads, for this atom count and geometry.  Host only,
  * no HIP call.  Returns 0 when the arguments are invalid or too large.
@@ -189,8 +230,8 @@ cpmap_status cpmap_bin_grid(int32_t nx, int32_t ny, int32_t nz, float spacing,
  *   bin_start  (nbins + 1) int32: bin b holds sorted[bin_start[b] ..
  *              bin_start[b+1]); bin_start[nbins] = kept atoms
  *   sorted     float4 atoms in bin order
- * (offsets of both: cpmap_workspace_layout).  Also records, on the host, the
- * geometry the workspace was binned for, so that cpmap_cutoff can check it.
+ * (offsets of both: cpmap_workspace_layout; a header occupies the first 256
+ * bytes).  Records the fill as "Workspace records" above describes.
  *
  *   atoms, n_atoms, nx..oz   as in cpmap_direct
  *   bin_size, cutoff         finite, > 0 (Angstrom)
@@ -233,7 +274,9 @@ cpmap_status cpmap_workspace_layout(int64_t n_atoms,
  *                                n_atoms and geometry; read only
  *   n_atoms, nx..cutoff          the values given to cpmap_bin_atoms
  *   V                            device, nx*ny*nz floats, written
- * Returns CPMAP_EGEOM if the workspace was not binned for these arguments.
+ * Returns CPMAP_EGEOM if the workspace was not binned for these arguments
+ * (its record, "Workspace records" above); V is all NaN if the workspace's
+ * header no longer matches that record.
  * Accuracy: |V - V_exact| <= 1e-5 * sum_{r < rc} |q| / r at every node.
  */
 cpmap_status cpmap_cutoff(const void *workspace, size_t workspace_bytes, int64_t n_atoms,
@@ -307,7 +350,8 @@ int64_t cpmap_neighbor_spans(int32_t nx, int32_t ny, int32_t nz, float spacing,
  * alternative layout for the cutoff sum, kept for measurement beside the CSR
  * (which never overflows).
  *
- * A slot workspace holds (byte offsets: cpmap_slot_layout):
+ * A slot workspace holds (byte offsets: cpmap_slot_layout; a header occupies
+ * the first 256 bytes):
  *   slots       float4[nbins * capacity]: slot s of bin b at b*capacity + s;
  *               an empty slot is (+inf, +inf, +inf, 0).  Empty slots are told
  *               apart by their position, never by a zero charge, so a neutral
@@ -351,10 +395,10 @@ cpmap_status cpmap_slot_layout(int64_t n_atoms,
  *                                bytes, 256-byte aligned, not overlapping
  *                                workspace (else CPMAP_EINVAL); overwritten
  *   slot_workspace_bytes         its size (else CPMAP_ENOSPC)
- * Records, on the host, the geometry and capacity the slot workspace was
- * filled for, so that cpmap_cutoff_slots can check them.  Five stream-ordered
- * launches; the result is the same on every run.  Ownership: caller owns
- * both workspaces; they must stay valid until the work on them completes.
+ * Records the fill (geometry and capacity) as "Workspace records" above
+ * describes.  Six stream-ordered launches; the result is the same on every
+ * run.  Ownership: caller owns both workspaces; they must stay valid until
+ * the work on them completes.
  */
 cpmap_status cpmap_bin_slots(const void *workspace, size_t workspace_bytes, int64_t n_atoms,
                              int32_t nx, int32_t ny, int32_t nz, float spacing,
@@ -400,9 +444,8 @@ size_t cpmap_extrema_workspace_bytes(int64_t n);
  * Writes, on the device, out_index[0] = argmin and out_index[1] = argmax of
  * V[0..n) and out_value[0..1] = the values there.  NaN values are skipped;
  * among equal values the smallest index wins (+0 and -0 are equal); with no
- * non-NaN value both indices are -1 and both values NaN.  A linear index of
- * a lattice map gives the node as i = idx % nx, j = (idx / nx) % ny,
- * k = idx / (nx * ny).
+ * non-NaN value both indices are -1 and both values NaN.  For a lattice map,
+ * cpmap_node_position turns an index into its node and position.
  *
  *   V          device, n floats (any layout; read only)
  *   out_index  device, 2 int64 (8-byte aligned), written

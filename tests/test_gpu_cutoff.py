@@ -370,3 +370,115 @@ def test_binding_rejects_bad_buffers(torch):
     idx, val = cpmap.extrema(V, out=(torch.empty(2, dtype=torch.int64, device="cuda"),
                                      torch.empty(2, device="cuda")))
     assert val.tolist() == [0.0, 0.0]
+
+
+# ---------------------------------------------------------------- workspace records
+
+def _small_binned(torch, n=2000, seed=31):
+    lat = Lattice(20, 18, 16, 0.5)
+    atoms_np = wl.random_atoms(n, (-2, -2, -2), (12, 11, 10), seed=seed)
+    atoms = torch.from_numpy(atoms_np).cuda()
+    return lat, atoms_np, atoms
+
+
+def test_workspace_overwritten_outside_the_library_gives_nan(torch):
+    """A binned workspace whose header bytes changed since binning (here
+    zeroed by torch) is not read: every node of V is NaN.  Rebinning it
+    restores the map.  The same holds for a slot workspace built from it."""
+    lat, atoms_np, atoms = _small_binned(torch)
+    n = atoms_np.shape[0]
+    ws = cpmap.bin_atoms(atoms, lat, 1.0, 3.0)
+    good = cpmap.cutoff(ws, n, lat, 1.0, 3.0).clone()
+    ws[:16].zero_()
+    V = cpmap.cutoff(ws, n, lat, 1.0, 3.0)
+    torch.cuda.synchronize()
+    assert torch.isnan(V).all().item()
+    Vt = cpmap.cutoff(ws, n, lat, 1.0, 3.0, term="truncated")
+    assert torch.isnan(Vt).all().item()
+    # slots built from the damaged workspace are refused by the cutoff kernels
+    sws = cpmap.bin_slots(ws, n, lat, 1.0, 3.0, 4)
+    Vs = cpmap.cutoff_slots(sws, n, lat, 1.0, 3.0, 4)
+    torch.cuda.synchronize()
+    assert torch.isnan(Vs).all().item()
+    cpmap.bin_atoms(atoms, lat, 1.0, 3.0, workspace=ws)
+    assert torch.equal(cpmap.cutoff(ws, n, lat, 1.0, 3.0), good)
+    # a damaged slot header alone (capacity 4 overflows here, so the slot
+    # map is compared with itself, not bit for bit with the CSR map)
+    sws = cpmap.bin_slots(ws, n, lat, 1.0, 3.0, 4)
+    slot_good = cpmap.cutoff_slots(sws, n, lat, 1.0, 3.0, 4).clone()
+    torch.testing.assert_close(slot_good, good, rtol=1e-5, atol=1e-5)
+    sws[8:16].fill_(1)
+    assert torch.isnan(cpmap.cutoff_slots(sws, n, lat, 1.0, 3.0, 4)).all().item()
+
+
+def test_writes_through_the_library_drop_overlapping_records(torch):
+    """Any entry point that writes device memory drops the records of the
+    workspaces it overlaps: rebinning through another base address, using the
+    workspace as the direct sum's scratch or as an output, and the extrema
+    outputs; afterwards the cutoff call returns CPMAP_EGEOM.  A workspace
+    next to the written range keeps its record."""
+    lat, atoms_np, atoms = _small_binned(torch)
+    n = atoms_np.shape[0]
+    need = cpmap.bin_workspace_bytes(n, lat, 1.0, 3.0)
+    big = torch.empty(3 * need + 4096, dtype=torch.uint8, device="cuda")
+    a = big[:need]
+    b = big[need + 256: 2 * need + 256]   # after a, not touching it
+    cpmap.bin_atoms(atoms, lat, 1.0, 3.0, workspace=a)
+    cpmap.bin_atoms(atoms, lat, 1.0, 3.0, workspace=b)
+    ref = cpmap.cutoff(a, n, lat, 1.0, 3.0).clone()
+
+    def refused(ws):
+        with pytest.raises(cpmap.CpmapError) as e:
+            cpmap.cutoff(ws, n, lat, 1.0, 3.0)
+        return e.value.status == 4
+
+    # rebinning at an address inside a
+    cpmap.bin_atoms(atoms, lat, 1.0, 3.0, workspace=big[256:256 + need])
+    assert refused(a)
+    assert torch.equal(cpmap.cutoff(b, n, lat, 1.0, 3.0), ref)  # b kept its record
+    # the direct sum's output written over b's tail
+    cpmap.bin_atoms(atoms, lat, 1.0, 3.0, workspace=a)
+    assert torch.equal(cpmap.cutoff(a, n, lat, 1.0, 3.0), ref)
+    small = Lattice(4, 4, 4, 0.5)
+    out = big[2 * need:2 * need + 256].view(torch.float32).view(4, 4, 4)
+    cpmap.direct(atoms[:10], small, out=out, split=False)
+    assert refused(b)
+    assert torch.equal(cpmap.cutoff(a, n, lat, 1.0, 3.0), ref)
+    # the extrema outputs over a's first bytes
+    idx = big[1024:1040].view(torch.int64)
+    val = big[2048:2056].view(torch.float32)
+    cpmap.extrema(ref.reshape(-1), out=(idx, val))
+    assert refused(a)
+    # a cutoff output over the workspace itself
+    cpmap.bin_atoms(atoms, lat, 1.0, 3.0, workspace=b)
+    cpmap.bin_atoms(atoms, lat, 1.0, 3.0, workspace=a)
+    V = b[:256].view(torch.float32).view(4, 4, 4)
+    cpmap.direct(atoms[:10], small, out=V, split=False)
+    assert refused(b)
+    assert torch.equal(cpmap.cutoff(a, n, lat, 1.0, 3.0), ref)
+
+
+def test_reused_workspace_memory_is_refused_or_nan(torch):
+    """A binned workspace freed and its memory handed to a new tensor that is
+    then filled outside the library: the cutoff call either finds no record
+    (CPMAP_EGEOM, new address) or finds the stale record and the kernel sees
+    the changed header (NaN at every node) -- never a map computed from the
+    new contents."""
+    lat, atoms_np, atoms = _small_binned(torch)
+    n = atoms_np.shape[0]
+    need = cpmap.bin_workspace_bytes(n, lat, 1.0, 3.0)
+    ws = cpmap.bin_atoms(atoms, lat, 1.0, 3.0)
+    addr = ws.data_ptr()
+    torch.cuda.synchronize()
+    del ws
+    ws2 = torch.empty(need, dtype=torch.uint8, device="cuda")
+    ws2.fill_(7)
+    try:
+        V = cpmap.cutoff(ws2, n, lat, 1.0, 3.0)
+    except cpmap.CpmapError as e:
+        assert e.status == 4
+        assert ws2.data_ptr() != addr
+    else:
+        torch.cuda.synchronize()
+        assert ws2.data_ptr() == addr
+        assert torch.isnan(V).all().item()

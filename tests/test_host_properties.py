@@ -54,10 +54,10 @@ def test_bin_and_slot_layouts_are_consistent(nx, ny, nz, h, ox, oy, oz, bs, rc, 
     # just below H when the lattice is a single node thick)
     assert all(d >= 2 * halo for d in o_dims)
     assert nbins < 2**31
-    assert nbytes >= 4 * (nbins + 1) + 16 * n
+    assert nbytes >= 256 + 4 * (nbins + 1) + 16 * n
     a, b = ctypes.c_int64(), ctypes.c_int64()
     assert lib.cpmap_workspace_layout(n, *L, bs, rc, ctypes.byref(a), ctypes.byref(b)) == OK
-    assert a.value == 0 and b.value >= 4 * (nbins + 1) and b.value % 256 == 0
+    assert a.value == 256 and b.value >= a.value + 4 * (nbins + 1) and b.value % 256 == 0
     assert b.value + 16 * n <= nbytes
     # fixed-capacity slots
     sbytes = lib.cpmap_slot_workspace_bytes(n, *L, bs, rc, cap)
@@ -68,8 +68,8 @@ def test_bin_and_slot_layouts_are_consistent(nx, ny, nz, h, ox, oy, oz, bs, rc, 
         assert st_slot == ERANGE and sbytes == 0
         return
     assert st_slot == OK and sbytes > 0
-    assert s.value == 0
-    assert o.value >= 16 * nbins * cap and o.value % 256 == 0
+    assert s.value == 256
+    assert o.value >= s.value + 16 * nbins * cap and o.value % 256 == 0
     assert v.value >= o.value + 4 * (nbins + 1) and v.value % 256 == 0
     assert v.value + 16 * n <= sbytes
 
