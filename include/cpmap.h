@@ -432,7 +432,7 @@ cpmap_status cpmap_cutoff_slots(const void *slot_workspace, size_t slot_workspac
 
 /*
  * cpmap_extrema_workspace_bytes -- workspace of cpmap_extrema for n values
- * (at most 64 KB).  Host only, no HIP call; 0 on invalid n.
+ * (at most 16 KB).  Host only, no HIP call; 0 on invalid n.
  */
 size_t cpmap_extrema_workspace_bytes(int64_t n);
 
@@ -450,7 +450,12 @@ size_t cpmap_extrema_workspace_bytes(int64_t n);
  *   V          device, n floats (any layout; read only)
  *   out_index  device, 2 int64 (8-byte aligned), written
  *   out_value  device, 2 floats, written
- *   workspace  device, >= cpmap_extrema_workspace_bytes(n), 256-byte aligned
+ *   workspace  device, >= cpmap_extrema_workspace_bytes(n), 256-byte aligned;
+ *              needs no clearing (its contents before the call do not matter)
+ * One launch: each workgroup publishes a partial result tagged with a number
+ * drawn for this call, and the last workgroup waits for all of them (a
+ * bounded wait; an index of -2 would report that it ran out, which ordinary
+ * runs never do).  Two calls that overlap on the same workspace race.
  * Deterministic: the result does not depend on the order in which partial
  * results are combined.
  */

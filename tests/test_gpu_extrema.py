@@ -94,3 +94,24 @@ def test_place_ions_on_a_potential_map(torch):
         assert abs(v - Vo[g]) <= 1e-5 * S[g]
         assert pos == (float(np.float32(i * np.float32(0.5))), float(np.float32(j * np.float32(0.5))),
                        float(np.float32(k * np.float32(0.5))))
+
+
+@pytest.mark.parametrize("n", [5, 20_000, 8_000_000, 16_711_681])
+def test_extrema_needs_no_cleared_workspace(torch, n):
+    """The one-launch reduction keeps a tagged counter in its workspace: a
+    workspace full of arbitrary bytes, and the same workspace reused call
+    after call with maps of different sizes (the grid, and so the count the
+    last workgroup waits for, changes), give the oracle's answer every time.
+    16,711,681 nodes take the largest grid (512 workgroups, two slabs
+    each)."""
+    rng = np.random.default_rng(n)
+    ws = torch.randint(0, 256, (cpmap.library().cpmap_extrema_workspace_bytes(16_711_681),),
+                       dtype=torch.uint8, device="cuda")
+    for m in (n, max(n // 3, 1), n):
+        V_np = rng.standard_normal(m).astype(np.float32)
+        V_np[rng.integers(0, m, size=max(m // 100, 1))] = np.nan
+        V = torch.from_numpy(V_np).cuda()
+        idx, val = cpmap.extrema(V, workspace=ws)
+        torch.cuda.synchronize()
+        (oi, ov) = oracle.extrema(V_np)
+        assert tuple(idx.cpu().tolist()) == oi
