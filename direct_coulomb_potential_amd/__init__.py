@@ -26,7 +26,7 @@ __all__ = [
     "bin_grid", "workspace_layout", "workspace_views", "neighbor_spans", "library",
     "library_path", "header_functions", "STATUS", "extrema", "place_ions", "TERMS",
     "slot_workspace_bytes", "slot_layout", "bin_slots", "slot_views", "cutoff_slots",
-    "node_position",
+    "node_position", "extrema_noalloc",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -77,6 +77,7 @@ _SIGNATURES = {
     "cpmap_bin_slots": (_i32, [_vp, _sz, _i64, *_LAT, _f32, _f32, _i32, _vp, _sz, _vp]),
     "cpmap_cutoff_slots": (_i32, [_vp, _sz, _i64, *_LAT, _f32, _f32, _i32, _i32, _vp, _vp]),
     "cpmap_node_position": (_i32, [*_LAT, _i64, ctypes.POINTER(_i32), ctypes.POINTER(_f32)]),
+    "cpmap_extrema_noalloc": (_i32, [_vp, _i64, _vp, _vp, _vp]),
 }
 
 
@@ -407,6 +408,25 @@ def extrema(V, workspace=None, out=None):
         val = _buffer(out[1], torch.float32, V.device, "out[1]", 2)
     _call("cpmap_extrema", V.device, V.data_ptr() if n else None, n, idx.data_ptr(),
           val.data_ptr(), workspace.data_ptr(), workspace.numel())
+    return idx, val
+
+
+def extrema_noalloc(V, out=None):
+    """cpmap_extrema_noalloc: as extrema(), with the library's static
+    per-device scratch instead of a workspace (nothing is allocated when
+    `out` is given); calls that overlap on one GPU race."""
+    torch = _torch()
+    if V.dtype != torch.float32 or not V.is_cuda or not V.is_contiguous():
+        raise ValueError("V must be a contiguous float32 GPU tensor")
+    n = V.numel()
+    if out is None:
+        idx = torch.empty(2, dtype=torch.int64, device=V.device)
+        val = torch.empty(2, dtype=torch.float32, device=V.device)
+    else:
+        idx = _buffer(out[0], torch.int64, V.device, "out[0]", 2)
+        val = _buffer(out[1], torch.float32, V.device, "out[1]", 2)
+    _call("cpmap_extrema_noalloc", V.device, V.data_ptr() if n else None, n, idx.data_ptr(),
+          val.data_ptr())
     return idx, val
 
 

@@ -554,4 +554,24 @@ cpmap_status cpmap_extrema(const float *V, int64_t n, int64_t *out_index, float 
     return e == hipSuccess ? CPMAP_OK : CPMAP_EHIP;
 }
 
+cpmap_status cpmap_extrema_noalloc(const float *V, int64_t n, int64_t *out_index,
+                                   float *out_value, void *stream)
+{
+    if (n < 0)
+        return CPMAP_EINVAL;
+    if (n > CPMAP_MAX_POINTS)
+        return CPMAP_ERANGE;
+    if ((n > 0 && V == nullptr) || out_index == nullptr || out_value == nullptr)
+        return CPMAP_EINVAL;
+    if (!aligned(V, 4) || !aligned(out_index, 8) || !aligned(out_value, 4))
+        return CPMAP_EINVAL;
+    if (extrema_workspace_bytes(n) > extrema_static_scratch_bytes())
+        return CPMAP_ERANGE;
+    g_registry.forget(out_index, 2 * sizeof(int64_t));
+    g_registry.forget(out_value, 2 * sizeof(float));
+    hipError_t e =
+        launch_extrema_static(V, n, out_index, out_value, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? CPMAP_OK : CPMAP_EHIP;
+}
+
 }  // extern "C"

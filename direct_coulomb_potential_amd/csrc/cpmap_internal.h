@@ -138,6 +138,10 @@ hipError_t launch_scatter(const float4 *atoms, int64_t n_atoms, const Lattice &l
 size_t extrema_workspace_bytes(int64_t n);
 hipError_t launch_extrema(const float *V, int64_t n, int64_t *out_index, float *out_value,
                           void *workspace, hipStream_t stream);
+// The same launch with the library's static per-device scratch as workspace.
+size_t extrema_static_scratch_bytes();
+hipError_t launch_extrema_static(const float *V, int64_t n, int64_t *out_index,
+                                 float *out_value, hipStream_t stream);
 
 // Nodes per tile edge of the cutoff kernel.
 constexpr int kTile = 8;

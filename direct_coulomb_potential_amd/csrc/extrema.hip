@@ -26,7 +26,9 @@
 // publishes its slot unconditionally and none waits on the combiner.
 #include <atomic>
 #include <chrono>
+#include <mutex>
 #include <random>
+#include <vector>
 
 #include "cpmap_internal.h"
 
@@ -300,7 +302,15 @@ uint64_t next_tag()
 
 }  // namespace
 
+// The allocation-free variant's slots: one copy per GPU, allocated when the
+// library is loaded and held until the process ends, zero at load (tag 0: no
+// call).  In host code this name is only a stand-in for the device address,
+// which static_scratch() looks up.
+static __device__ __align__(256) Slot scratch[kMaxBlocks];
+
 size_t extrema_workspace_bytes(int64_t n) { return sizeof(Slot) * (size_t)extrema_blocks(n); }
+
+size_t extrema_static_scratch_bytes() { return sizeof(scratch); }
 
 hipError_t launch_extrema(const float *V, int64_t n, int64_t *out_index, float *out_value,
                           void *workspace, hipStream_t stream)
@@ -311,6 +321,43 @@ hipError_t launch_extrema(const float *V, int64_t n, int64_t *out_index, float *
                        (int32_t)vec4, next_tag(), static_cast<Slot *>(workspace), out_index,
                        out_value);
     return hipGetLastError();
+}
+
+// Device address of the current device's copy of `scratch`: looked up with
+// hipGetSymbolAddress the first time a device calls, with that device
+// current, and kept per device.
+static hipError_t static_scratch(void **out)
+{
+    static std::mutex mu;
+    static std::vector<void *> per_device;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    std::lock_guard<std::mutex> lock(mu);
+    if ((size_t)dev >= per_device.size())
+        per_device.resize((size_t)dev + 1, nullptr);
+    if (per_device[(size_t)dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        per_device[(size_t)dev] = p;
+    }
+    *out = per_device[(size_t)dev];
+    return hipSuccess;
+}
+
+hipError_t launch_extrema_static(const float *V, int64_t n, int64_t *out_index,
+                                 float *out_value, hipStream_t stream)
+{
+    if (extrema_workspace_bytes(n) > sizeof(scratch))
+        return hipErrorInvalidValue;  // cannot happen: the grid never exceeds kMaxBlocks
+    void *slots = nullptr;
+    hipError_t e = static_scratch(&slots);
+    if (e != hipSuccess)
+        return e;
+    return launch_extrema(V, n, out_index, out_value, slots, stream);
 }
 
 }  // namespace cpmap

@@ -462,6 +462,28 @@ size_t cpmap_extrema_workspace_bytes(int64_t n);
 cpmap_status cpmap_extrema(const float *V, int64_t n, int64_t *out_index, float *out_value,
                            void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * cpmap_extrema_noalloc -- cpmap_extrema without a workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).
+ *
+ * The same kernel as cpmap_extrema, with its scratch (512 slots of 32 bytes,
+ * 16 KB) in a static device array of the library: one copy per GPU, allocated
+ * when the library is loaded and held until the process ends.  The call
+ * allocates and frees nothing.  Every call on one GPU shares that GPU's copy,
+ * which needs no clearing between calls (each call tags its slots with a
+ * fresh number); calls that overlap in time on one GPU (several streams or
+ * host threads) race and may give wrong results.  Any n up to
+ * CPMAP_MAX_POINTS fits the fixed scratch (the grid is capped at 512
+ * workgroups); larger n is CPMAP_ERANGE.
+ *
+ *   V, n, out_index, out_value, stream   as cpmap_extrema
+ * Errors as cpmap_extrema; CPMAP_EHIP also when the scratch's device address
+ * cannot be looked up.
+ */
+cpmap_status cpmap_extrema_noalloc(const float *V, int64_t n, int64_t *out_index,
+                                   float *out_value, void *stream);
+
 #ifdef __cplusplus
 }
 #endif
