@@ -1,7 +1,8 @@
 """Benchmark of the potential-map hot path on one MI355X.
 
 One step = one direct-sum call (cpmap_direct_with_workspace: atoms also split
-across workgroups into partial maps) over the 200^3 lattice (0.5 A) with
+across workgroups, their sums added into V in part order) over the 200^3
+lattice (0.5 A) with
 200,000 uniform atoms (charges U[-1,1] shifted to net zero): 1.6e12
 atom-node evaluations.  After the timed direct steps the same run times the cutoff path
 (cpmap_bin_atoms + cpmap_cutoff) on the 100k-atom, rc = 12 A, 4 A-bin system
@@ -212,7 +213,7 @@ def main():
             "traffic": measured_traffic("direct_kernel_200cube_200k.md",
                                         "direct_coulomb_potential_amd/csrc/direct.hip"),
             "traffic_unit": "bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated)",
-            "kernel": "direct_kernel (+ sum_parts, the partial-map add, inside the same events)",
+            "kernel": "direct_kernel (+ chain_reset, the split's counter clear, inside the same events)",
             "kernel_ms_mean": kern_ms,
             "kernel_ms_median": statistics.median(per),
             "kernel_ms_min": min(per),

@@ -22,12 +22,21 @@
 //    rounding growth for large same-sign atom sets, the fixed order keeps the
 //    result deterministic, and W fills the 1024 SIMDs for small lattices.
 //  - with a caller-provided workspace the atom list is also split into K
-//    contiguous parts across workgroups: each (part, node group) workgroup
-//    writes a partial map, and a second kernel adds the K maps in part order.
-//    The extra workgroups even out the last round of the 1024 SIMDs (977
-//    groups of 64 lanes x 128 nodes on a 200^3 lattice leave 5% of it idle)
-//    and keep the atom slices that run together small enough to share the
-//    scalar and L2 caches; the result stays deterministic.
+//    contiguous parts across workgroups, and the parts of a node group are
+//    added into V in part order, in place: part 0 stores its sum, part p
+//    waits until part p - 1 of the same group has added its own and then adds
+//    its sum to V.  Each workgroup takes a ticket from a counter when it
+//    starts, and the ticket (not the workgroup's index) names its part and
+//    group, parts in order; a part's predecessor therefore started before it
+//    and waits only on its own predecessor, so every wait ends (the wait is
+//    also bounded: a part that ran out of it writes NaN, which no ordinary
+//    run does).  Tickets are G apart for the two parts, so the predecessor
+//    has long finished when its successor gets to its store.  Short atom
+//    slices per workgroup run some 8% faster than whole-atom-list ones (VALU
+//    busy 107% against 98% in the counters) and the extra workgroups even out
+//    the last round of the 1024 SIMDs; the workspace holds only the counter
+//    and one count per group, and the result is deterministic (the same
+//    order of fp32 additions on every run).
 //  - nodes are stored x-fastest, V[(k*ny + j)*nx + i] (section 18.4) from the
 //    LDS total; lanes adjacent in x write adjacent 4*CX-byte runs.
 #include <algorithm>
@@ -71,26 +80,40 @@ __device__ __forceinline__ void accumulate_atom(const float4 a, const float (&x)
     }
 }
 
-// Workgroup b handles node group b % n_groups against atom part b / n_groups
-// and writes its nodes into out + part * part_stride (V itself when there is
-// one part, else the part's partial map in the workspace).
+// The ordered split's state in the workspace: chain[0] counts the
+// workgroups that have started; chain[kChainHead + g] counts the parts of
+// node group g already added into V.
+constexpr int kChainHead = 64;
+
+// Workgroup ticket t (its index when chain is null, else its place among the
+// started workgroups) handles node group t % n_groups against atom part
+// t / n_groups and adds its nodes into V in part order.
 template <int CX, int CY, int CZ, int W>
 __global__ __launch_bounds__(kWave *W) void direct_kernel(
     const float4 *__restrict__ atoms, int64_t n_atoms, int32_t nx, int32_t ny, int32_t nz,
-    int32_t nsx, int32_t nsy, int64_t n_strips, int64_t n_groups, int32_t n_parts,
-    int64_t part_stride, float h, float ox, float oy, float oz, float *__restrict__ out_base)
+    int32_t nsx, int32_t nsy, int64_t n_strips, int64_t n_groups, int32_t n_parts, float h,
+    float ox, float oy, float oz, uint32_t *__restrict__ chain, int64_t max_polls,
+    float *__restrict__ V)
 {
     constexpr int NP = CX * CY * CZ;
     __shared__ float total[NP * kWave];
+    __shared__ uint32_t s_ticket;
+    __shared__ int s_in_order;
 
     const int slice = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x % kWave;
 
+    uint32_t ticket = blockIdx.x;
+    if (chain != nullptr) {
+        if (threadIdx.x == 0)
+            s_ticket = atomicAdd(&chain[0], 1u);
+        __syncthreads();
+        ticket = s_ticket;
+    }
     // Lane -> block of nodes.  Lanes past the last block recompute the last
     // block (they still take part in the reduction) and store nothing.
-    const int64_t group = (int64_t)blockIdx.x % n_groups;
-    const int32_t part = (int32_t)((int64_t)blockIdx.x / n_groups);
-    float *__restrict__ V = out_base + (int64_t)part * part_stride;
+    const int64_t group = (int64_t)ticket % n_groups;
+    const int32_t part = (int32_t)((int64_t)ticket / n_groups);
     const int64_t s_raw = group * kWave + lane;
     const bool live = s_raw < n_strips;
     const int64_t s = live ? s_raw : n_strips - 1;
@@ -182,22 +205,53 @@ __global__ __launch_bounds__(kWave *W) void direct_kernel(
         }
     }
     __syncthreads();
-    if (!live)
-        return;
 
-    // x-fastest store from the LDS total; the waves share the rows.  Columns
-    // past nx, rows past ny and planes past nz are dropped.
-    for (int row = slice; row < CY * CZ; row += W) {
-        const int32_t j = j0 + row % CY;
-        const int32_t k = k0 + row / CY;
-        if (j >= ny || k >= nz)
-            continue;
-        float *out = V + ((int64_t)k * ny + j) * nx;
-        const float *src = total + row * CX * kWave + lane;
+    // Parts after the first wait for their predecessor's addition into V.
+    uint32_t *done = chain != nullptr ? chain + kChainHead + group : nullptr;
+    bool in_order = true;
+    if (done != nullptr) {
+        if (threadIdx.x == 0) {
+            int64_t polls = 0;
+            while (__hip_atomic_load(done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) !=
+                       (uint32_t)part &&
+                   polls < max_polls) {
+                __builtin_amdgcn_s_sleep(8);
+                ++polls;
+            }
+            s_in_order = polls < max_polls;
+        }
+        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        in_order = s_in_order != 0;
+    }
+
+    // x-fastest store (part 0) or addition (later parts) of the LDS total;
+    // the waves share the rows.  Columns past nx, rows past ny and planes past
+    // nz are dropped.
+    if (live) {
+        const bool add = done != nullptr && part > 0;
+        for (int row = slice; row < CY * CZ; row += W) {
+            const int32_t j = j0 + row % CY;
+            const int32_t k = k0 + row / CY;
+            if (j >= ny || k >= nz)
+                continue;
+            float *out = V + ((int64_t)k * ny + j) * nx;
+            const float *src = total + row * CX * kWave + lane;
 #pragma unroll
-        for (int c = 0; c < CX; ++c)
-            if (i0 + c < nx)
-                out[i0 + c] = src[c * kWave];
+            for (int c = 0; c < CX; ++c) {
+                if (i0 + c < nx) {
+                    const float v = add ? out[i0 + c] + src[c * kWave] : src[c * kWave];
+                    out[i0 + c] = in_order ? v : __builtin_nanf("");
+                }
+            }
+        }
+    }
+    if (done != nullptr) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __syncthreads();
+        if (threadIdx.x == 0)
+            __hip_atomic_store(done, (uint32_t)part + 1, __ATOMIC_RELEASE,
+                               __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -208,21 +262,17 @@ __global__ void fill_zero(float *__restrict__ V, int64_t n)
         V[i] = 0.0f;
 }
 
-// V[i] = sum over parts k = 0, 1, ... of part[k * n + i], in that order.
-__global__ void sum_parts(const float *__restrict__ parts, int32_t n_parts, int64_t n,
-                          float *__restrict__ V)
+// Clears the ordered split's counter and per-group counts.
+__global__ void chain_reset(uint32_t *__restrict__ chain, int64_t n_words)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
-        float v = parts[i];
-        for (int32_t k = 1; k < n_parts; ++k)
-            v += parts[(int64_t)k * n + i];
-        V[i] = v;
-    }
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_words; i += stride)
+        chain[i] = 0u;
 }
 
 using KernelFn = void (*)(const float4 *, int64_t, int32_t, int32_t, int32_t, int32_t, int32_t,
-                          int64_t, int64_t, int32_t, int64_t, float, float, float, float, float *);
+                          int64_t, int64_t, int32_t, float, float, float, float, uint32_t *,
+                          int64_t, float *);
 
 struct Variant {
     int cx, cy, cz, w;
@@ -242,9 +292,15 @@ const Variant kVariants[] = {
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 constexpr int kMaxParts = 32;
-constexpr double kMaxPartBytes = 1u << 30;  // cap on the partial maps of one call
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int64_t variant_groups(const Variant &v, const Lattice &lat)
+{
+    const int64_t strips = ceil_div(lat.n[0], v.cx) * ceil_div(lat.n[1], v.cy) *
+                           ceil_div(lat.n[2], v.cz);
+    return ceil_div(strips, kWave);
+}
 
 struct Plan {
     int variant;
@@ -263,7 +319,7 @@ struct Plan {
 //    hides less latency: at half the occupancy it runs ~7% slower (measured
 //    on the 8x4x2 variant, whose occupancy is 4);
 //  - one issue slot of a wave is 4 cycles at 2.4 GHz;
-//  - with parts > 1, the partial maps are written once and summed once.
+//  - with parts > 1, every part reads and writes its nodes of V once.
 double plan_seconds(const Variant &v, int32_t parts, const Lattice &lat, int64_t n_atoms)
 {
     const int64_t strips = ceil_div(lat.n[0], v.cx) * ceil_div(lat.n[1], v.cy) *
@@ -283,7 +339,7 @@ double plan_seconds(const Variant &v, int32_t parts, const Lattice &lat, int64_t
     }
     double t = units * wave_work * 4.0 / 2.4e9;
     if (parts > 1)
-        t += (2.0 * parts + 1.0) * 4.0 * (double)lat.points() / 8.0e12 + 3e-6;
+        t += 2.0 * parts * 4.0 * (double)lat.points() / 8.0e12 + 3e-6;
     return t;
 }
 
@@ -293,12 +349,12 @@ Plan make_plan(const Lattice &lat, int64_t n_atoms, bool allow_parts)
     const int max_parts = allow_parts ? kMaxParts : 1;
     for (int i = 0; i < kNumVariants; ++i) {
         for (int32_t k = 1; k <= max_parts; ++k) {
-            if (k > 1 && (double)k * 4.0 * (double)lat.points() > kMaxPartBytes)
-                break;
+            if (k > 1 && variant_groups(kVariants[i], lat) * k > (int64_t)INT32_MAX)
+                break;  // tickets and the grid stay below 2^31
             if (k > 1 && n_atoms < (int64_t)k * kVariants[i].w * 64)
                 break;  // keep at least 64 atoms per wave
             const double t = plan_seconds(kVariants[i], k, lat, n_atoms);
-            // prefer fewer parts (less workspace) unless clearly faster
+            // prefer fewer parts unless clearly faster
             if (t < best.seconds * (k > best.parts ? 0.995 : 1.0)) {
                 best = Plan{i, k, t};
             }
@@ -307,9 +363,13 @@ Plan make_plan(const Lattice &lat, int64_t n_atoms, bool allow_parts)
     return best;
 }
 
+// The ordered split's counter and per-group counts, in 256-byte units.
 size_t plan_workspace(const Plan &p, const Lattice &lat)
 {
-    return p.parts > 1 ? (size_t)p.parts * (size_t)lat.points() * sizeof(float) : 0;
+    if (p.parts <= 1)
+        return 0;
+    const size_t words = kChainHead + (size_t)variant_groups(kVariants[p.variant], lat);
+    return (words * sizeof(uint32_t) + 255) & ~size_t(255);
 }
 
 }  // namespace
@@ -365,15 +425,26 @@ hipError_t launch_direct(const float4 *atoms, int64_t n_atoms, const Lattice &la
     const int64_t nsz = ceil_div(lat.n[2], v.cz);
     const int64_t strips = (int64_t)nsx * nsy * nsz;
     const int64_t groups = ceil_div(strips, kWave);
-    float *out = plan.parts > 1 ? static_cast<float *>(workspace) : V;
+    uint32_t *chain = nullptr;
+    int64_t max_polls = 0;
+    if (plan.parts > 1) {
+        // A part waits at most about as long as its predecessor's task runs
+        // (it started later on equal work): bound the wait at ten modelled
+        // task times, at least 2^26 polls of s_sleep(8) (about 14 s).
+        const double np = v.cx * v.cy * v.cz;
+        const double per_pair = 4.0 + (v.cx + v.cy + 2.0 * v.cz + v.cy * v.cz) / np;
+        const double task_s = std::ceil((double)n_atoms / ((double)plan.parts * v.w)) * np *
+                              per_pair * 4.0 * v.occupancy / 2.0e9;
+        max_polls = std::max<int64_t>(1ll << 26, (int64_t)std::min(1e15, 10.0 * task_s / 2.0e-7));
+        chain = static_cast<uint32_t *>(workspace);
+        const int64_t words = kChainHead + groups;
+        hipLaunchKernelGGL(chain_reset, dim3((unsigned)std::min<int64_t>(ceil_div(words, 256), 64)),
+                           dim3(256), 0, stream, chain, words);
+    }
     hipLaunchKernelGGL(v.kernel, dim3((unsigned)(groups * plan.parts)), dim3(kWave * v.w), 0,
                        stream, atoms, n_atoms, lat.n[0], lat.n[1], lat.n[2], nsx, nsy, strips,
-                       groups, plan.parts, points, lat.h, lat.o[0], lat.o[1], lat.o[2], out);
-    if (plan.parts > 1) {
-        const int64_t blocks = std::min<int64_t>(ceil_div(points, 256), 8192);
-        hipLaunchKernelGGL(sum_parts, dim3((unsigned)blocks), dim3(256), 0, stream, out,
-                           plan.parts, points, V);
-    }
+                       groups, plan.parts, lat.h, lat.o[0], lat.o[1], lat.o[2], chain, max_polls,
+                       V);
     return hipGetLastError();
 }
 

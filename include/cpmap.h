@@ -123,23 +123,29 @@ cpmap_status cpmap_direct_scatter(const float *atoms, int64_t n_atoms,
 /*
  * cpmap_direct_workspace_bytes -- size of the optional workspace that lets
  * cpmap_direct_with_workspace split the atom list across workgroups (0 when
- * the lattice and atom count gain nothing from it).  Host only, no HIP call;
- * depends only on n_atoms and the lattice dimensions.  0 on invalid input.
+ * the lattice and atom count gain nothing from it; a few KB otherwise: a
+ * counter and one count per group of 64 lanes' nodes).  Host only, no HIP
+ * call; depends only on n_atoms and the lattice dimensions.  0 on invalid
+ * input.
  */
 size_t cpmap_direct_workspace_bytes(int64_t n_atoms, int32_t nx, int32_t ny, int32_t nz);
 
 /*
  * cpmap_direct_with_workspace -- the same direct sum as cpmap_direct, with a
- * caller-owned scratch buffer.  The library may then also split the atoms
- * into K contiguous parts handled by different workgroups, write K partial
- * maps into the workspace and add them in part order (still no atomics,
- * still deterministic); on large lattices this evens out the last round of
- * workgroups over the GPU.  Results agree with cpmap_direct within the
- * accuracy bound (the summation order differs).
+ * small caller-owned workspace.  The library may then also split the atoms
+ * into K contiguous parts handled by different workgroups: part 0 of a group
+ * of nodes stores its sum into V, and part p adds its sum into V once part
+ * p - 1 has added its own (the workspace holds the counters that order them),
+ * so the additions happen in part order on every run (still no atomics on V,
+ * still deterministic).  On large lattices the short per-workgroup atom
+ * slices run faster and even out the last round of workgroups over the GPU.
+ * Results agree with cpmap_direct within the accuracy bound (the summation
+ * order differs).
  *
  *   workspace        device, >= cpmap_direct_workspace_bytes(...) bytes,
  *                    256-byte aligned (may be NULL when that size is 0);
- *                    overwritten, must stay valid until the work completes
+ *                    overwritten, must stay valid until the work completes;
+ *                    two calls that overlap on one workspace race
  *   workspace_bytes  its size; CPMAP_ENOSPC when too small
  * Other arguments, ownership and errors as cpmap_direct.
  */

@@ -220,10 +220,12 @@ def test_planner_picks_each_variant_for_its_test_geometry():
 def test_direct_workspace_queries_and_checks():
     lib = cpmap.library()
     need = lib.cpmap_direct_workspace_bytes(200_000, 200, 200, 200)
-    assert need > 0 and need % (4 * 200**3) == 0
+    # the 200^3 lattice at 8x8x2 nodes per lane: 977 node groups; the ordered
+    # split keeps a 64-word head and one count per group (4,352 bytes)
+    assert need == 4352
     assert lib.cpmap_direct_workspace_bytes(-1, 200, 200, 200) == 0
     assert lib.cpmap_direct_workspace_bytes(10, -1, 2, 2) == 0
-    assert cpmap.direct_plan(200_000, Lattice(200, 200, 200, 0.5), True)[4] == need // (4 * 200**3)
+    assert cpmap.direct_plan(200_000, Lattice(200, 200, 200, 0.5), True) == (8, 8, 2, 4, 11)
     assert cpmap.direct_plan(200_000, Lattice(200, 200, 200, 0.5), False)[4] == 1
     assert cpmap.direct_plan(1, Lattice(1, 1, 1, 0.5), True)[4] == 1
     assert lib.cpmap_direct_workspace_bytes(1, 1, 1, 1) == 0

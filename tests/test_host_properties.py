@@ -112,12 +112,15 @@ def test_direct_plans_are_compiled_variants_with_bounded_workspace(nx, ny, nz, n
     if not ws:
         assert plan[4] == 1
     need = lib.cpmap_direct_workspace_bytes(n, nx, ny, nz)
-    points = nx * ny * nz
     with_ws = (ctypes.c_int32 * 5)()
     lib.cpmap_direct_plan(n, nx, ny, nz, 1, with_ws)
     if with_ws[4] > 1:
-        assert need == with_ws[4] * 4 * points
-        assert need <= 1 << 30
+        # the ordered split's counter and one count per node group, 256-byte units
+        cx, cy, cz = with_ws[0], with_ws[1], with_ws[2]
+        strips = -(-nx // cx) * -(-ny // cy) * -(-nz // cz)
+        groups = -(-strips // 64)
+        assert need == -(-(4 * (64 + groups)) // 256) * 256
+        assert groups * with_ws[4] < 2**31
         assert n >= with_ws[4] * with_ws[3] * 64  # at least 64 atoms per wave
     else:
         assert need == 0
