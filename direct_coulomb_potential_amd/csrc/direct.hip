@@ -22,21 +22,28 @@
 //    rounding growth for large same-sign atom sets, the fixed order keeps the
 //    result deterministic, and W fills the 1024 SIMDs for small lattices.
 //  - with a caller-provided workspace the atom list is also split into K
-//    contiguous parts across workgroups, and the parts of a node group are
-//    added into V in part order, in place: part 0 stores its sum, part p
-//    waits until part p - 1 of the same group has added its own and then adds
-//    its sum to V.  Each workgroup takes a ticket from a counter when it
-//    starts, and the ticket (not the workgroup's index) names its part and
-//    group, parts in order; a part's predecessor therefore started before it
-//    and waits only on its own predecessor, so every wait ends (the wait is
-//    also bounded: a part that ran out of it writes NaN, which no ordinary
-//    run does).  Tickets are G apart for the two parts, so the predecessor
-//    has long finished when its successor gets to its store.  Short atom
-//    slices per workgroup run some 8% faster than whole-atom-list ones (VALU
-//    busy 107% against 98% in the counters) and the extra workgroups even out
-//    the last round of the 1024 SIMDs; the workspace holds only the counter
-//    and one count per group, and the result is deterministic (the same
-//    order of fp32 additions on every run).
+//    contiguous parts across workgroups (short atom slices per workgroup run
+//    some 8% faster than whole-atom-list ones: VALU busy 107% against 98% in
+//    the counters; and the extra workgroups even out the last round of the
+//    1024 SIMDs).  The parts of a node group are added in part order, in one
+//    of two ways:
+//      ordered   (at least as many node groups as resident workgroups) in
+//                place: part 0 stores its sum, part p waits until part p - 1
+//                of the same group has added its own and then adds its sum
+//                to V.  Each workgroup takes a ticket from a counter when it
+//                starts, and the ticket (not the workgroup's index) names its
+//                part and group, parts in order; a part's predecessor
+//                therefore started before it and waits only on its own
+//                predecessor, so every wait ends (it is also bounded: a part
+//                that ran out of it writes NaN, which no ordinary run does).
+//                Tickets are G apart for the two parts, so the predecessor
+//                has long finished when its successor gets to its store; the
+//                workspace is the counter and one count per group.
+//      partial   (fewer groups: all parts run at once, and ordered additions
+//                would queue) part 0 stores into V and part p into partial
+//                map p - 1 of the workspace; sum_parts then adds the maps
+//                into V in part order.
+//    Either way the fp32 additions happen in the same order on every run.
 //  - nodes are stored x-fastest, V[(k*ny + j)*nx + i] (section 18.4) from the
 //    LDS total; lanes adjacent in x write adjacent 4*CX-byte runs.
 #include <algorithm>
@@ -85,14 +92,22 @@ __device__ __forceinline__ void accumulate_atom(const float4 a, const float (&x)
 // node group g already added into V.
 constexpr int kChainHead = 64;
 
-// Workgroup ticket t (its index when chain is null, else its place among the
-// started workgroups) handles node group t % n_groups against atom part
-// t / n_groups and adds its nodes into V in part order.
-template <int CX, int CY, int CZ, int W>
-__global__ __launch_bounds__(kWave *W) void direct_kernel(
+// How the parts of a node group are added (see the file comment).
+enum SplitMode { kSingle = 0, kOrdered = 1, kPartial = 2 };
+
+// Workgroup ticket t (its index unless the split is ordered, else its place
+// among the started workgroups) handles node group t % n_groups against atom
+// part t / n_groups.  Its nodes go to V (part 0, or every part when ordered)
+// or, for a partial split, to partial map part - 1 in the workspace.  The
+// workspace is the ordered split's counters (uint32) or the partial maps
+// (nx*ny*nz floats each).
+// OCC is the resident waves per SIMD the variant is planned for; the
+// compiler keeps its registers within that budget.
+template <int CX, int CY, int CZ, int W, int OCC>
+__global__ __launch_bounds__(kWave *W) __attribute__((amdgpu_waves_per_eu(OCC))) void direct_kernel(
     const float4 *__restrict__ atoms, int64_t n_atoms, int32_t nx, int32_t ny, int32_t nz,
     int32_t nsx, int32_t nsy, int64_t n_strips, int64_t n_groups, int32_t n_parts, float h,
-    float ox, float oy, float oz, uint32_t *__restrict__ chain, int64_t max_polls,
+    float ox, float oy, float oz, int32_t mode, void *__restrict__ ws, int64_t max_polls,
     float *__restrict__ V)
 {
     constexpr int NP = CX * CY * CZ;
@@ -103,6 +118,7 @@ __global__ __launch_bounds__(kWave *W) void direct_kernel(
     const int slice = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x % kWave;
 
+    uint32_t *chain = mode == kOrdered ? static_cast<uint32_t *>(ws) : nullptr;
     uint32_t ticket = blockIdx.x;
     if (chain != nullptr) {
         if (threadIdx.x == 0)
@@ -230,12 +246,15 @@ __global__ __launch_bounds__(kWave *W) void direct_kernel(
     // nz are dropped.
     if (live) {
         const bool add = done != nullptr && part > 0;
+        float *dst = (mode == kPartial && part > 0)
+                         ? static_cast<float *>(ws) + (int64_t)(part - 1) * nx * ny * nz
+                         : V;
         for (int row = slice; row < CY * CZ; row += W) {
             const int32_t j = j0 + row % CY;
             const int32_t k = k0 + row / CY;
             if (j >= ny || k >= nz)
                 continue;
-            float *out = V + ((int64_t)k * ny + j) * nx;
+            float *out = dst + ((int64_t)k * ny + j) * nx;
             const float *src = total + row * CX * kWave + lane;
 #pragma unroll
             for (int c = 0; c < CX; ++c) {
@@ -262,6 +281,20 @@ __global__ void fill_zero(float *__restrict__ V, int64_t n)
         V[i] = 0.0f;
 }
 
+// V[i] += partial maps 1, 2, ... at i, in that order (partial map k - 1 of
+// `partials` holds part k).
+__global__ void sum_parts(const float *__restrict__ partials, int32_t n_maps, int64_t n,
+                          float *__restrict__ V)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        float v = V[i];
+        for (int32_t k = 0; k < n_maps; ++k)
+            v += partials[(int64_t)k * n + i];
+        V[i] = v;
+    }
+}
+
 // Clears the ordered split's counter and per-group counts.
 __global__ void chain_reset(uint32_t *__restrict__ chain, int64_t n_words)
 {
@@ -271,7 +304,7 @@ __global__ void chain_reset(uint32_t *__restrict__ chain, int64_t n_words)
 }
 
 using KernelFn = void (*)(const float4 *, int64_t, int32_t, int32_t, int32_t, int32_t, int32_t,
-                          int64_t, int64_t, int32_t, float, float, float, float, uint32_t *,
+                          int64_t, int64_t, int32_t, float, float, float, float, int32_t, void *,
                           int64_t, float *);
 
 struct Variant {
@@ -280,7 +313,8 @@ struct Variant {
     KernelFn kernel;
 };
 
-#define CPMAP_VARIANT(CX, CY, CZ, W, OCC) Variant{CX, CY, CZ, W, OCC, direct_kernel<CX, CY, CZ, W>}
+#define CPMAP_VARIANT(CX, CY, CZ, W, OCC) \
+    Variant{CX, CY, CZ, W, OCC, direct_kernel<CX, CY, CZ, W, OCC>}
 
 // Occupancies (resident waves per SIMD) are those of the gfx950 build (183,
 // 111, 67, 54, 41 and 29 VGPRs; LDS never limits); a GPU test checks them
@@ -302,6 +336,21 @@ int64_t variant_groups(const Variant &v, const Lattice &lat)
     return ceil_div(strips, kWave);
 }
 
+// Workgroups of a variant resident on the 256 CUs at once.
+int64_t resident_workgroups(const Variant &v)
+{
+    return 256 * std::max(1, v.occupancy * 4 / v.w);
+}
+
+SplitMode split_mode(const Variant &v, int32_t parts, const Lattice &lat)
+{
+    if (parts <= 1)
+        return kSingle;
+    return variant_groups(v, lat) >= resident_workgroups(v) ? kOrdered : kPartial;
+}
+
+constexpr double kMaxPartialBytes = 64.0 * (1 << 20);  // cap on partial maps
+
 struct Plan {
     int variant;
     int32_t parts;
@@ -319,7 +368,9 @@ struct Plan {
 //    hides less latency: at half the occupancy it runs ~7% slower (measured
 //    on the 8x4x2 variant, whose occupancy is 4);
 //  - one issue slot of a wave is 4 cycles at 2.4 GHz;
-//  - with parts > 1, every part reads and writes its nodes of V once.
+//  - with parts > 1, every part reads and writes its nodes of V once
+//    (ordered), or the parts' maps are written once and summed once
+//    (partial).
 double plan_seconds(const Variant &v, int32_t parts, const Lattice &lat, int64_t n_atoms)
 {
     const int64_t strips = ceil_div(lat.n[0], v.cx) * ceil_div(lat.n[1], v.cy) *
@@ -339,7 +390,9 @@ double plan_seconds(const Variant &v, int32_t parts, const Lattice &lat, int64_t
     }
     double t = units * wave_work * 4.0 / 2.4e9;
     if (parts > 1)
-        t += 2.0 * parts * 4.0 * (double)lat.points() / 8.0e12 + 3e-6;
+        t += (split_mode(v, parts, lat) == kOrdered ? 2.0 * parts : 2.0 * parts + 1.0) * 4.0 *
+                 (double)lat.points() / 8.0e12 +
+             3e-6;
     return t;
 }
 
@@ -351,6 +404,9 @@ Plan make_plan(const Lattice &lat, int64_t n_atoms, bool allow_parts)
         for (int32_t k = 1; k <= max_parts; ++k) {
             if (k > 1 && variant_groups(kVariants[i], lat) * k > (int64_t)INT32_MAX)
                 break;  // tickets and the grid stay below 2^31
+            if (split_mode(kVariants[i], k, lat) == kPartial &&
+                (double)(k - 1) * 4.0 * (double)lat.points() > kMaxPartialBytes)
+                break;
             if (k > 1 && n_atoms < (int64_t)k * kVariants[i].w * 64)
                 break;  // keep at least 64 atoms per wave
             const double t = plan_seconds(kVariants[i], k, lat, n_atoms);
@@ -363,13 +419,23 @@ Plan make_plan(const Lattice &lat, int64_t n_atoms, bool allow_parts)
     return best;
 }
 
-// The ordered split's counter and per-group counts, in 256-byte units.
+// The ordered split's counter and per-group counts, or the partial maps of
+// parts 1 .. K-1, in 256-byte units.
 size_t plan_workspace(const Plan &p, const Lattice &lat)
 {
-    if (p.parts <= 1)
+    const Variant &v = kVariants[p.variant];
+    size_t bytes = 0;
+    switch (split_mode(v, p.parts, lat)) {
+    case kSingle:
         return 0;
-    const size_t words = kChainHead + (size_t)variant_groups(kVariants[p.variant], lat);
-    return (words * sizeof(uint32_t) + 255) & ~size_t(255);
+    case kOrdered:
+        bytes = (kChainHead + (size_t)variant_groups(v, lat)) * sizeof(uint32_t);
+        break;
+    case kPartial:
+        bytes = (size_t)(p.parts - 1) * (size_t)lat.points() * sizeof(float);
+        break;
+    }
+    return (bytes + 255) & ~size_t(255);
 }
 
 }  // namespace
@@ -425,9 +491,9 @@ hipError_t launch_direct(const float4 *atoms, int64_t n_atoms, const Lattice &la
     const int64_t nsz = ceil_div(lat.n[2], v.cz);
     const int64_t strips = (int64_t)nsx * nsy * nsz;
     const int64_t groups = ceil_div(strips, kWave);
-    uint32_t *chain = nullptr;
     int64_t max_polls = 0;
-    if (plan.parts > 1) {
+    const SplitMode mode = split_mode(v, plan.parts, lat);
+    if (mode == kOrdered) {
         // A part waits at most about as long as its predecessor's task runs
         // (it started later on equal work): bound the wait at ten modelled
         // task times, at least 2^26 polls of s_sleep(8) (about 14 s).
@@ -436,15 +502,20 @@ hipError_t launch_direct(const float4 *atoms, int64_t n_atoms, const Lattice &la
         const double task_s = std::ceil((double)n_atoms / ((double)plan.parts * v.w)) * np *
                               per_pair * 4.0 * v.occupancy / 2.0e9;
         max_polls = std::max<int64_t>(1ll << 26, (int64_t)std::min(1e15, 10.0 * task_s / 2.0e-7));
-        chain = static_cast<uint32_t *>(workspace);
+        uint32_t *chain = static_cast<uint32_t *>(workspace);
         const int64_t words = kChainHead + groups;
         hipLaunchKernelGGL(chain_reset, dim3((unsigned)std::min<int64_t>(ceil_div(words, 256), 64)),
                            dim3(256), 0, stream, chain, words);
     }
     hipLaunchKernelGGL(v.kernel, dim3((unsigned)(groups * plan.parts)), dim3(kWave * v.w), 0,
                        stream, atoms, n_atoms, lat.n[0], lat.n[1], lat.n[2], nsx, nsy, strips,
-                       groups, plan.parts, lat.h, lat.o[0], lat.o[1], lat.o[2], chain, max_polls,
-                       V);
+                       groups, plan.parts, lat.h, lat.o[0], lat.o[1], lat.o[2], (int32_t)mode,
+                       mode == kSingle ? nullptr : workspace, max_polls, V);
+    if (mode == kPartial) {
+        const int64_t blocks = std::min<int64_t>(ceil_div(points, 256), 8192);
+        hipLaunchKernelGGL(sum_parts, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           static_cast<const float *>(workspace), plan.parts - 1, points, V);
+    }
     return hipGetLastError();
 }
 

@@ -123,8 +123,10 @@ cpmap_status cpmap_direct_scatter(const float *atoms, int64_t n_atoms,
 /*
  * cpmap_direct_workspace_bytes -- size of the optional workspace that lets
  * cpmap_direct_with_workspace split the atom list across workgroups (0 when
- * the lattice and atom count gain nothing from it; a few KB otherwise: a
- * counter and one count per group of 64 lanes' nodes).  Host only, no HIP
+ * the lattice and atom count gain nothing from it).  On lattices with at
+ * least as many groups of 64 lanes' nodes as the GPU holds workgroups at
+ * once, a few KB (a counter and one count per group); on smaller lattices,
+ * K - 1 partial maps of the lattice, at most 64 MiB.  Host only, no HIP
  * call; depends only on n_atoms and the lattice dimensions.  0 on invalid
  * input.
  */
@@ -133,12 +135,15 @@ size_t cpmap_direct_workspace_bytes(int64_t n_atoms, int32_t nx, int32_t ny, int
 /*
  * cpmap_direct_with_workspace -- the same direct sum as cpmap_direct, with a
  * small caller-owned workspace.  The library may then also split the atoms
- * into K contiguous parts handled by different workgroups: part 0 of a group
- * of nodes stores its sum into V, and part p adds its sum into V once part
- * p - 1 has added its own (the workspace holds the counters that order them),
- * so the additions happen in part order on every run (still no atomics on V,
- * still deterministic).  On large lattices the short per-workgroup atom
- * slices run faster and even out the last round of workgroups over the GPU.
+ * into K contiguous parts handled by different workgroups.  On large
+ * lattices part 0 of a group of nodes stores its sum into V, and part p adds
+ * its sum into V once part p - 1 has added its own (the workspace holds the
+ * counters that order them); on small lattices, where all parts run at
+ * once, parts 1..K-1 write partial maps into the workspace that a second
+ * kernel adds to V in part order.  Either way the additions happen in part
+ * order on every run (no atomics on V, deterministic).  The short
+ * per-workgroup atom slices run faster and even out the last round of
+ * workgroups over the GPU.
  * Results agree with cpmap_direct within the accuracy bound (the summation
  * order differs).
  *

@@ -14,8 +14,11 @@ import direct_coulomb_potential_amd as cpmap
 import oracle
 
 OK, EINVAL, ERANGE = 0, 1, 2
-VARIANTS = {(8, 8, 2, 4), (8, 8, 2, 8), (8, 4, 2, 4), (8, 4, 2, 8), (4, 4, 2, 8),
-            (4, 4, 2, 16), (4, 4, 1, 16), (2, 2, 1, 16), (1, 1, 1, 16)}
+# compiled direct-kernel variants (nodes per lane x, y, z; waves per
+# workgroup) and their resident waves per SIMD, as the planner's table has them
+OCCUPANCY = {(8, 8, 2, 4): 2, (8, 8, 2, 8): 2, (8, 4, 2, 4): 4, (8, 4, 2, 8): 4, (4, 4, 2, 8): 6,
+             (4, 4, 2, 16): 4, (4, 4, 1, 16): 8, (2, 2, 1, 16): 8, (1, 1, 1, 16): 8}
+VARIANTS = set(OCCUPANCY)
 
 dims = st.integers(1, 400)
 spacing = st.floats(0.05, 4.0)
@@ -115,13 +118,20 @@ def test_direct_plans_are_compiled_variants_with_bounded_workspace(nx, ny, nz, n
     with_ws = (ctypes.c_int32 * 5)()
     lib.cpmap_direct_plan(n, nx, ny, nz, 1, with_ws)
     if with_ws[4] > 1:
-        # the ordered split's counter and one count per node group, 256-byte units
-        cx, cy, cz = with_ws[0], with_ws[1], with_ws[2]
+        cx, cy, cz, w, k = with_ws
         strips = -(-nx // cx) * -(-ny // cy) * -(-nz // cz)
         groups = -(-strips // 64)
-        assert need == -(-(4 * (64 + groups)) // 256) * 256
-        assert groups * with_ws[4] < 2**31
-        assert n >= with_ws[4] * with_ws[3] * 64  # at least 64 atoms per wave
+        resident = 256 * max(1, OCCUPANCY[(cx, cy, cz, w)] * 4 // w)
+        if groups >= resident:
+            # ordered: the counter and one count per node group
+            want = 4 * (64 + groups)
+        else:
+            # partial: maps of parts 1 .. K-1, at most 64 MiB
+            want = 4 * (k - 1) * nx * ny * nz
+            assert want <= 64 << 20
+        assert need == -(-want // 256) * 256
+        assert groups * k < 2**31
+        assert n >= k * w * 64  # at least 64 atoms per wave
     else:
         assert need == 0
 
