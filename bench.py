@@ -31,6 +31,13 @@ PEAK_FP32_TFLOPS = 157.3   # MI355X fp32 vector peak (256 CU x 2.4 GHz x 256 FLO
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 PEAK_CLOCK_GHZ = 2.4       # engine clock the peak is quoted at
 FLOP_PER_EVAL = 10
+# Work of one in-cutoff atom-node pair of the cutoff kernel, counted as the
+# binning lecture's slide-24 term is written: the Coulomb part as the direct
+# sum's 10 FLOP, plus gamma(r^2) = GC0 + r^2 (GC1 + r^2 GC2) (two fused
+# multiply-adds, 4 FLOP) and its subtraction (1) for the smoothed term; the
+# hard-truncated term (the case-study section 18.5 listing) is the Coulomb
+# part alone.
+FLOP_PER_CUTOFF_PAIR = {"smoothed": 15, "truncated": 10}
 
 
 def profile_record(profile: str, source: str):
@@ -84,9 +91,11 @@ def parse():
                    help="also time the direct path on every lattice/atom configuration "
                         "(median and minimum of 10 after 3 warm-ups) and, in the CPU "
                         "baseline, the oracle on each configuration's checked nodes")
-    p.add_argument("--only", choices=["direct", "cutoff", "copy"], default=None,
+    p.add_argument("--only", choices=["direct", "cutoff", "copy", "small"], default=None,
                    help="time one path only (for profiler runs); 'copy' runs the plain "
-                        "256 MiB copy kernel that calibrates the HBM byte counters")
+                        "256 MiB copy kernel that calibrates the HBM byte counters; "
+                        "'small' the direct sum on the single plane and the 100x100x50 "
+                        "lattice (10,000 atoms each)")
     p.add_argument("--no-direct-compare", action="store_true",
                    help="skip the direct sum on the cutoff atoms (for profiler runs)")
     return p.parse_args()
@@ -164,6 +173,10 @@ def main():
         print(json.dumps({"copy_bytes_read": a.numel() * 4, "copy_bytes_written": b.numel() * 4}))
         return
 
+    if args.only == "small":
+        print(json.dumps(bench_small(torch, cpmap, wl, dev, args)))
+        return
+
     w = wl.large_direct()
     lat = w.lattice
     pairs = w.pairs
@@ -226,6 +239,18 @@ def main():
             # SIMD's VALU issue saturated; null once the source has changed)
             "valu_busy_pct_from_counters": prof.get("valu_busy_pct") if prof else None,
         }
+        # cpmap_direct, the call without a workspace (no atom split), on the
+        # same map: timed beside the headline (two launches after one warm-up)
+        _, per_plain = time_launches(torch, lambda: cpmap.direct(atoms, lat, out=V, split=False),
+                                     2, 1)
+        plain_ms = statistics.median(per_plain)
+        result["roofline"]["no_workspace"] = {
+            "entry_point": "cpmap_direct",
+            "plan": list(cpmap.direct_plan(w.n_atoms, lat, False)),
+            "kernel_ms_median": plain_ms,
+            "achieved": FLOP_PER_EVAL * pairs / (plain_ms * 1e-3) / 1e12,
+            "frac": FLOP_PER_EVAL * pairs / (plain_ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS,
+        }
         # ion placement on the map just computed: argmin / argmax over 8M nodes
         ext_ws = torch.empty(cpmap.library().cpmap_extrema_workspace_bytes(lat.n_points),
                              dtype=torch.uint8, device=dev)
@@ -259,6 +284,40 @@ def main():
             result["cpu_baseline"]["per_config"] = oracle_per_config(oracle, wl)
 
     print(json.dumps(result), flush=True)
+
+
+def bench_small(torch, cpmap, wl, dev, args):
+    """The direct sum on the two 10,000-atom workloads (the single plane k = 10
+    and the 100x100x50 lattice): event-timed launches (median, minimum) and
+    the same number of launches back to back between two events."""
+    out = {}
+    steps = max(args.steps, 20)
+    for w in (wl.plane_direct(), wl.full_direct()):
+        lat = w.lattice
+        atoms = torch.from_numpy(w.atoms).to(dev)
+        V = torch.empty((lat.nz, lat.ny, lat.nx), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(cpmap.direct_workspace_bytes(w.n_atoms, lat), 1), dtype=torch.uint8,
+                         device=dev)
+        fn = lambda: cpmap.direct(atoms, lat, out=V, workspace=ws)  # noqa: E731
+        _, per = time_launches(torch, fn, steps, args.warmup)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        med, b2b = statistics.median(per), a.elapsed_time(b) / steps
+        out[w.name] = {
+            "plan": list(cpmap.direct_plan(w.n_atoms, lat, True)),
+            "ms_median": med,
+            "ms_min": min(per),
+            "ms_back_to_back": b2b,
+            "pct_fp32_peak": 100.0 * FLOP_PER_EVAL * w.pairs / (med * 1e-3) / 1e12
+            / PEAK_FP32_TFLOPS,
+            "pct_fp32_peak_back_to_back": 100.0 * FLOP_PER_EVAL * w.pairs / (b2b * 1e-3) / 1e12
+            / PEAK_FP32_TFLOPS,
+        }
+    return out
 
 
 def bench_all_configs(torch, cpmap, wl, dev, clock):
@@ -414,6 +473,10 @@ def bench_cutoff(torch, cpmap, wl, dev, args):
         dir_ms = statistics.median(per_dir)
     bytes_alg = 16 * w.n_atoms + 4 * lat.n_points
     in_cut, in_cut_note = in_cutoff_pairs(w)
+    trunc_ms = statistics.median(per_trunc)
+
+    def tflops(term, ms):
+        return in_cut * FLOP_PER_CUTOFF_PAIR[term] / (ms * 1e-3) / 1e12
     prof = profile_record("cutoff_kernel_200cube_100k_rc12.md",
                           "direct_coulomb_potential_amd/csrc/cutoff.hip")
     examined = prof.get("pairs_evaluated") if prof else None
@@ -423,7 +486,21 @@ def bench_cutoff(torch, cpmap, wl, dev, args):
         "bin_ms_median": bin_ms,
         "cutoff_ms_median": cut_ms,
         "cutoff_ms_min": min(per_cut),
-        "truncated_term_ms_median": statistics.median(per_trunc),
+        "truncated_term_ms_median": trunc_ms,
+        # the cutoff kernel against the same fp32 vector peak, at the FLOP per
+        # in-cutoff pair above (event-timed kernel launches, median)
+        "roofline": {
+            "bound": "alu",
+            "achieved": tflops("smoothed", cut_ms),
+            "peak": PEAK_FP32_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": tflops("smoothed", cut_ms) / PEAK_FP32_TFLOPS,
+            "kernel": "cutoff_kernel (smoothed term)",
+            "flop_per_in_cutoff_pair": FLOP_PER_CUTOFF_PAIR["smoothed"],
+            "truncated_achieved": tflops("truncated", trunc_ms),
+            "truncated_frac": tflops("truncated", trunc_ms) / PEAK_FP32_TFLOPS,
+            "truncated_flop_per_in_cutoff_pair": FLOP_PER_CUTOFF_PAIR["truncated"],
+        },
         "end_to_end_ms_with_l2_flush": wall_e2e / steps * 1e3,
         "bin_plus_cutoff_ms_median": statistics.median(per_pair),
         "bin_plus_cutoff_hip_graph_ms_median": statistics.median(per_graph),
