@@ -101,10 +101,22 @@ def parse():
     return p.parse_args()
 
 
-def time_launches(torch, fn, steps, warmup):
-    """Run fn warmup times, then `steps` times between device syncs, each launch
-    bracketed by events on torch's current stream (the stream the library
-    launches on).  Returns (wall seconds of the timed region, per-launch ms)."""
+# Untimed calls before the side measurements: after the GPU has idled (host
+# work between sections), its engine clock needs some 20-40 ms of load to
+# rise again, and millisecond-scale launches timed right away read it rising.
+SETTLE_S = 0.25
+
+
+def time_launches(torch, fn, steps, warmup, settle_s=0.0):
+    """Call fn for settle_s seconds of wall time and then warmup more times,
+    untimed; then `steps` times between device syncs, each launch bracketed by
+    events on torch's current stream (the stream the library launches on).
+    Returns (wall seconds of the timed region, per-launch ms)."""
+    t_end = time.perf_counter() + settle_s
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -259,10 +271,18 @@ def main():
         _, per_ext = time_launches(torch, lambda: cpmap.extrema(V, workspace=ext_ws, out=ext_out),
                                    max(args.steps, 10), args.warmup)
         ext_ms = statistics.median(per_ext)
+        ext_prof = profile_record("extrema_kernel_200cube.md",
+                                  "direct_coulomb_potential_amd/csrc/extrema.hip")
+        ext_kernel_ms = ext_prof["kernel_median_ns"] * 1e-6 if ext_prof else None
         result["ion_placement"] = {
             "op": "argmin/argmax of V (cpmap_extrema)",
+            # event-timed call (includes the launch), and the kernel's own
+            # median duration from the committed trace (null once stale)
             "ms_median": ext_ms,
             "hbm_gbs_algorithmic": 4 * lat.n_points / (ext_ms * 1e-3) / 1e9,
+            "kernel_ms_from_trace": ext_kernel_ms,
+            "kernel_hbm_gbs_algorithmic": (4 * lat.n_points / (ext_kernel_ms * 1e-3) / 1e9
+                                           if ext_kernel_ms else None),
             "peak_gbs": PEAK_HBM_GBS,
         }
         del atoms, V, ws, ext_ws
@@ -299,7 +319,7 @@ def bench_small(torch, cpmap, wl, dev, args):
         ws = torch.empty(max(cpmap.direct_workspace_bytes(w.n_atoms, lat), 1), dtype=torch.uint8,
                          device=dev)
         fn = lambda: cpmap.direct(atoms, lat, out=V, workspace=ws)  # noqa: E731
-        _, per = time_launches(torch, fn, steps, args.warmup)
+        _, per = time_launches(torch, fn, steps, args.warmup, settle_s=SETTLE_S)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(steps):
@@ -453,9 +473,9 @@ def bench_cutoff(torch, cpmap, wl, dev, args):
         run_cut()
 
     steps = max(args.steps, 5)
-    _, per_bin = time_launches(torch, run_bin, steps, args.warmup)
-    _, per_cut = time_launches(torch, run_cut, steps, args.warmup)
-    _, per_trunc = time_launches(torch, run_trunc, steps, args.warmup)
+    _, per_bin = time_launches(torch, run_bin, steps, args.warmup, settle_s=SETTLE_S)
+    _, per_cut = time_launches(torch, run_cut, steps, args.warmup, settle_s=SETTLE_S)
+    _, per_trunc = time_launches(torch, run_trunc, steps, args.warmup, settle_s=SETTLE_S)
     wall_e2e, _ = time_launches(torch, run_both, steps, args.warmup)
     _, per_pair = time_launches(torch, lambda: (run_bin(), run_cut()), steps, args.warmup)
     graph = capture_graph(torch, lambda: (run_bin(), run_cut()))
