@@ -352,7 +352,7 @@ def bench_all_configs(torch, cpmap, wl, dev, clock):
         need = cpmap.direct_workspace_bytes(w.n_atoms, lat)
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
         _, per = time_launches(torch, lambda: cpmap.direct(atoms, lat, out=V, workspace=ws),
-                               10, 3)
+                               10, 3, settle_s=SETTLE_S)
         med = statistics.median(per)
         tflops = FLOP_PER_EVAL * w.pairs / (med * 1e-3) / 1e12
         out[w.name] = {
