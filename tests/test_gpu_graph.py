@@ -93,12 +93,17 @@ def test_graph_direct_and_extrema_replays(torch):
                       dtype=torch.uint8, device="cuda")
     idx = torch.empty(2, dtype=torch.int64, device="cuda")
     val = torch.empty(2, dtype=torch.float32, device="cuda")
+    idx1 = torch.empty(2, dtype=torch.int64, device="cuda")
+    val1 = torch.empty(2, dtype=torch.float32, device="cuda")
     atoms.copy_(torch.from_numpy(wl.random_atoms(n, (-5, -8, -5), (25, 12, 12), seed=65)))
 
     def path():
         cpmap.direct(atoms, lat, out=V, workspace=wsd)
         cpmap.direct(atoms, lat, out=V1, split=False)
         cpmap.extrema(V, workspace=exw, out=(idx, val))
+        # the static per-GPU slots of the allocation-free entry point, which
+        # a replay (same tag) must also find cleared
+        cpmap.extrema_noalloc(V1, out=(idx1, val1))
 
     g = _capture(torch, path)
     for seed in _seeds():
@@ -107,13 +112,15 @@ def test_graph_direct_and_extrema_replays(torch):
         atoms.copy_(torch.from_numpy(atoms_np))
         g.replay()
         torch.cuda.synchronize()
-        got = [V.clone(), V1.clone(), idx.clone(), val.clone()]
+        got = [V.clone(), V1.clone(), idx.clone(), val.clone(), idx1.clone(), val1.clone()]
         path()
         torch.cuda.synchronize()
-        for a, b in zip(got, [V, V1, idx, val]):
+        for a, b in zip(got, [V, V1, idx, val, idx1, val1]):
             assert torch.equal(a, b)
     Vo, S = oracle.direct(atoms_np, lat.dims, lat.spacing, lat.origin, with_scale=True)
     err = np.abs(got[0].cpu().numpy().reshape(-1).astype(np.float64) - Vo)
     assert np.all(err <= 1e-5 * S)
     (imin, imax), _ = oracle.extrema(got[0].cpu().numpy())
     assert got[2].cpu().tolist() == [imin, imax]
+    (imin, imax), _ = oracle.extrema(got[1].cpu().numpy())
+    assert got[4].cpu().tolist() == [imin, imax]
