@@ -567,6 +567,17 @@ cpmap_status cpmap_extrema_noalloc(const float *V, int64_t n, int64_t *out_index
         return CPMAP_EINVAL;
     if (extrema_workspace_bytes(n) > extrema_static_scratch_bytes())
         return CPMAP_ERANGE;
+    // the scratch is the current device's copy: the stream must run there
+    int current = 0;
+    if (hipGetDevice(&current) != hipSuccess)
+        return CPMAP_EHIP;
+    if (stream != nullptr) {
+        hipDevice_t owner = 0;
+        if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &owner) != hipSuccess)
+            return CPMAP_EHIP;
+        if ((int)owner != current)
+            return CPMAP_EINVAL;
+    }
     g_registry.forget(out_index, 2 * sizeof(int64_t));
     g_registry.forget(out_value, 2 * sizeof(float));
     hipError_t e =

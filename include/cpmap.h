@@ -486,7 +486,9 @@ cpmap_status cpmap_extrema(const float *V, int64_t n, int64_t *out_index, float 
  * fresh number); calls that overlap in time on one GPU (several streams or
  * host threads) race and may give wrong results.  Any n up to
  * CPMAP_MAX_POINTS fits the fixed scratch (the grid is capped at 512
- * workgroups); larger n is CPMAP_ERANGE.
+ * workgroups); larger n is CPMAP_ERANGE.  The copy used is the current
+ * device's (hipGetDevice), so the stream must belong to that device; a
+ * stream of another device is CPMAP_EINVAL.
  *
  *   V, n, out_index, out_value, stream   as cpmap_extrema
  * Errors as cpmap_extrema; CPMAP_EHIP also when the scratch's device address
