@@ -168,17 +168,28 @@ __global__ __launch_bounds__(kThreads) void k_scatter(
     const int t = threadIdx.x;
     const int wave = t / 64;
     const int lane = t % 64;
+    const int64_t base = (int64_t)blockIdx.x * kTileElems;
+    // the tile's keys and values are loaded at once, with the tile's digit
+    // offsets, before the sub-tiles' barriers (one memory latency instead of
+    // one per sub-tile)
+    int32_t keys_r[kItems], vals_r[kItems];
+#pragma unroll
+    for (int it = 0; it < kItems; ++it) {
+        const int64_t e = base + it * kThreads + t;
+        keys_r[it] = e < n ? keys_in[e] : 0;
+        vals_r[it] = e < n ? vals_in[e] : 0;
+    }
     run[t] = offsets[(int64_t)t * n_tiles + blockIdx.x];
     for (int w = 0; w < kWaves; ++w)
         wave_cnt[w][t] = 0;
     __syncthreads();
     const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-    const int64_t base = (int64_t)blockIdx.x * kTileElems;
+#pragma unroll
     for (int it = 0; it < kItems; ++it) {
         const int64_t e = base + it * kThreads + t;
         const bool valid = e < n;
-        const int32_t key = valid ? keys_in[e] : 0;
-        const int32_t val = valid ? vals_in[e] : 0;
+        const int32_t key = keys_r[it];
+        const int32_t val = vals_r[it];
         const int d = valid ? (key >> shift) & 0xff : kDigits;  // invalid lanes: own class
         // lanes of this wave holding the same digit (invalid lanes match none)
         uint64_t same = __ballot(valid);
