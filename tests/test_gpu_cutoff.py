@@ -51,6 +51,9 @@ BIN_CASES = [
     (5000, Lattice(30, 30, 30, 0.3, (-4.0, 0.0, 2.0)), 1.0, 2.5, (-8, -4, -2), (8, 13, 14), 3),
     (70_000, Lattice(64, 48, 40, 0.5), 2.0, 6.0, (-10, -10, -10), (42, 34, 30), 4),
     (3000, Lattice(200, 200, 200, 0.5), 0.25, 12.0, (0, 0, 0), (100, 100, 100), 5),  # 3 radix passes
+    # 196 radix tiles: the digit scan's 50,176 counts take four rounds of
+    # 16,384, the last one partial, linked by the carry
+    (400_000, Lattice(64, 48, 40, 0.5), 1.0, 3.0, (-4, -4, -4), (36, 28, 24), 8),
 ]
 
 
