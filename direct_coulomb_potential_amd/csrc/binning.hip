@@ -13,8 +13,8 @@
 //             formed by the first pass's histogram kernel
 //   per pass  tile histograms -> one exclusive scan (digit-major) -> stable
 //             scatter, ranking equal digits inside a wave with ballots
-//   starts    bin_start[b] = lower_bound(sorted keys, b)
-//   gather    sorted atoms = atoms[sorted indices]
+//   finish    one launch, two jobs: bin_start[b] = lower_bound(sorted keys,
+//             b), and sorted atoms = atoms[sorted indices]
 #include "cpmap_internal.h"
 
 namespace cpmap {
