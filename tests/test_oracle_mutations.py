@@ -75,6 +75,16 @@ MUTATIONS = [
      "const double gamma = gc0 + r2 * (gc1 + r2 * gc2 * 1.0001);"),
     ("smoothed term: gamma added, not subtracted", "return q * (1.0 / sqrt(r2) - gamma);",
      "return q * (1.0 / sqrt(r2) + gamma);"),
+    ("smoothed term: GC0", "const double gc0 = 15.0 / (8.0 * rc);",
+     "const double gc0 = 16.0 / (8.0 * rc);"),
+    ("direct: charge sign", "v += q / r;", "v -= q / r;"),
+    ("node index: z decode", "*k = g / ((int64_t)nx * (int64_t)ny);",
+     "*k = g / ((int64_t)nx * (int64_t)nx);"),
+    ("binning: reversed order inside a bin",
+     "const int64_t dst = (int64_t)bin_start[ids[a]] + fill[ids[a]]++;",
+     "const int64_t dst = (int64_t)bin_start[ids[a] + 1] - 1 - fill[ids[a]]++;"),
+    ("binning: atoms on the grid's lower face dropped", "if (!(t >= 0.0f && t < (float)dims[d]))",
+     "if (!(t > 0.0f && t < (float)dims[d]))"),
 ]
 
 
