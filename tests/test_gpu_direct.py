@@ -134,6 +134,36 @@ def test_direct_same_sign_charges_large_n(torch, split):
     print(f"same-sign worst |err|/S = {worst:.3e}")
 
 
+@pytest.mark.parametrize("split", [False, True])
+def test_atom_on_a_node_gives_infinity(torch, split):
+    """An atom exactly on a node (at the node's fp32 position) makes that
+    node's potential +inf (positive charge) or -inf (negative), as the
+    boundary documents; every other node stays finite and meets the bound,
+    in the direct sum and in both cutoff terms."""
+    lat = Lattice(23, 17, 11, 0.5, (1.0, -2.0, 0.25))
+    atoms_np = wl.random_atoms(300, (0, -3, -1), (12, 7, 6), seed=71)
+    on = {1234: 0.75, 2500: -0.5}  # node index -> charge of the atom placed on it
+    for g, q in on.items():
+        _, xyz = cpmap.node_position(lat, g)
+        atoms_np = np.vstack([atoms_np, np.array([[*xyz, q]], dtype=np.float32)])
+    Vg = _run_direct(torch, atoms_np, lat, split=split)
+    keep = np.ones(lat.n_points, dtype=bool)
+    for g, q in on.items():
+        assert Vg[g] == (np.inf if q > 0 else -np.inf), (g, Vg[g])
+        keep[g] = False
+    Vo, S = oracle.direct(atoms_np, lat.dims, lat.spacing, lat.origin, with_scale=True)
+    _assert_parity(Vg[keep], Vo[keep], S[keep], "atoms on nodes, direct")
+    atoms = torch.from_numpy(np.ascontiguousarray(atoms_np)).cuda()
+    ws = cpmap.bin_atoms(atoms, lat, 2.0, 4.0)
+    for term, fn in (("smoothed", oracle.cutoff), ("truncated", oracle.cutoff_hard)):
+        Vc = cpmap.cutoff(ws, atoms_np.shape[0], lat, 2.0, 4.0, term=term).cpu().numpy()
+        Vc = Vc.reshape(-1)
+        for g, q in on.items():
+            assert Vc[g] == (np.inf if q > 0 else -np.inf), (term, g, Vc[g])
+        Vo, S = fn(atoms_np, lat.dims, lat.spacing, lat.origin, 4.0, with_scale=True)
+        _assert_parity(Vc[keep], Vo[keep], S[keep], f"atoms on nodes, cutoff {term}")
+
+
 @pytest.mark.parametrize("split", [False, True], ids=["plain", "split"])
 def test_direct_is_deterministic(torch, split):
     atoms = torch.from_numpy(wl.random_atoms(50_000, (0, 0, 0), (20, 20, 20), seed=12)).cuda()
