@@ -184,9 +184,10 @@ constexpr int kGroups = 64 / kGroupLanes;              // 4 cubes per wave
 constexpr int kStage = 256;                            // atoms staged per chunk (4 KB)
 constexpr int kMaxRows = 256;                          // (cy, cz) rows per list chunk
 // Resident waves per SIMD the kernel is built for: the sweep is latency-bound
-// on its LDS reads below this (measured 1.74 ms at 4 waves, 1.66 ms at 5 on
-// the 100k-atom rc = 12 A map).  LDS per workgroup (about 14 KB: the stage
-// and eight lists of kStage entries) allows 5 as well.
+// on its LDS reads below this (on the 100k-atom rc = 12 A map, built for 4
+// waves: 1.51 / 1.46 ms for the smoothed / truncated term, against 1.45 /
+// 1.38 ms at 5).  LDS per workgroup (about 14 KB: the stage and eight lists
+// of kStage entries) allows 5 as well.
 constexpr int kWavesPerSimd = 5;
 
 // kRsqInside serves atoms within the cutoff of every node of the wave, which
