@@ -98,6 +98,9 @@ def parse():
                         "lattice (10,000 atoms each)")
     p.add_argument("--no-direct-compare", action="store_true",
                    help="skip the direct sum on the cutoff atoms (for profiler runs)")
+    p.add_argument("--settle", type=float, default=SETTLE_S,
+                   help="seconds of untimed calls before each side measurement; profiler "
+                        "runs pass 0 so that every launch sequence has a fixed length")
     return p.parse_args()
 
 
@@ -295,7 +298,8 @@ def main():
 
     if args.all_configs and args.only is None:
         result["configs"] = bench_all_configs(torch, cpmap, wl, dev,
-                                              result["roofline"].get("clock_ghz_measured"))
+                                              result["roofline"].get("clock_ghz_measured"),
+                                              args.settle)
 
     if not args.no_cpu_baseline and args.only is None:
         import oracle
@@ -319,7 +323,7 @@ def bench_small(torch, cpmap, wl, dev, args):
         ws = torch.empty(max(cpmap.direct_workspace_bytes(w.n_atoms, lat), 1), dtype=torch.uint8,
                          device=dev)
         fn = lambda: cpmap.direct(atoms, lat, out=V, workspace=ws)  # noqa: E731
-        _, per = time_launches(torch, fn, steps, args.warmup, settle_s=SETTLE_S)
+        _, per = time_launches(torch, fn, steps, args.warmup, settle_s=args.settle)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(steps):
@@ -340,7 +344,7 @@ def bench_small(torch, cpmap, wl, dev, args):
     return out
 
 
-def bench_all_configs(torch, cpmap, wl, dev, clock):
+def bench_all_configs(torch, cpmap, wl, dev, clock, settle_s):
     """The direct path on workloads 1-4 and on the cutoff workload's atoms:
     hipEvent-timed, 3 warm-ups, then the median and minimum of 10 calls."""
     out = {}
@@ -352,7 +356,7 @@ def bench_all_configs(torch, cpmap, wl, dev, clock):
         need = cpmap.direct_workspace_bytes(w.n_atoms, lat)
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
         _, per = time_launches(torch, lambda: cpmap.direct(atoms, lat, out=V, workspace=ws),
-                               10, 3, settle_s=SETTLE_S)
+                               10, 3, settle_s=settle_s)
         med = statistics.median(per)
         tflops = FLOP_PER_EVAL * w.pairs / (med * 1e-3) / 1e12
         out[w.name] = {
@@ -473,9 +477,9 @@ def bench_cutoff(torch, cpmap, wl, dev, args):
         run_cut()
 
     steps = max(args.steps, 5)
-    _, per_bin = time_launches(torch, run_bin, steps, args.warmup, settle_s=SETTLE_S)
-    _, per_cut = time_launches(torch, run_cut, steps, args.warmup, settle_s=SETTLE_S)
-    _, per_trunc = time_launches(torch, run_trunc, steps, args.warmup, settle_s=SETTLE_S)
+    _, per_bin = time_launches(torch, run_bin, steps, args.warmup, settle_s=args.settle)
+    _, per_cut = time_launches(torch, run_cut, steps, args.warmup, settle_s=args.settle)
+    _, per_trunc = time_launches(torch, run_trunc, steps, args.warmup, settle_s=args.settle)
     wall_e2e, _ = time_launches(torch, run_both, steps, args.warmup)
     _, per_pair = time_launches(torch, lambda: (run_bin(), run_cut()), steps, args.warmup)
     graph = capture_graph(torch, lambda: (run_bin(), run_cut()))
