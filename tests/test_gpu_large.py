@@ -146,3 +146,97 @@ def test_direct_at_the_largest_axis(torch, free_after):
     with pytest.raises(cpmap.CpmapError):
         cpmap.direct(atoms, Lattice((1 << 24) + 1, 1, 1, 0.25))
     del V
+
+
+def _positions_bins(torch, starts64, kept, nbins, p0, p1):
+    """Bin of each sorted position in [p0, p1): the b with starts[b] <= p <
+    starts[b + 1], and nbins for the dropped atoms past the kept ones."""
+    pos = torch.arange(p0, p1, dtype=torch.int64, device="cuda")
+    b = torch.searchsorted(starts64, pos, right=True) - 1
+    return torch.where(pos < kept, b, torch.full_like(b, nbins))
+
+
+@pytest.mark.parametrize("n", [5_000_003, 2**31 - 1], ids=["n5M", "n_max"])
+def test_bin_atoms_at_the_largest_atom_count(torch, free_after, n):
+    """n_atoms up to CPMAP_MAX_ATOMS (2^31 - 1): sorted positions, tile
+    counts and bin starts reach the top of int32.  Each atom's charge carries
+    its input index as raw bits, so every sorted atom names its origin;
+    every 1000th atom lies outside the bin grid and is dropped.  Checked at
+    every position: the sorted atoms are the input atoms, bit for bit, each
+    input index once; bin starts rise from 0 to the kept count; every kept
+    atom lies in the box of the bin its position falls in (up to the bin
+    coordinate's rounding), dropped atoms sit past the kept ones, and equal
+    bins keep input order.  At sampled positions the oracle's own bin of the
+    input atom must contain the position."""
+    lat, bs, rc = Lattice(200, 200, 200, 0.5), 1.0, 3.0  # 106^3 bins: 3 radix passes
+    bd, b0, _ = oracle.bin_grid(lat.dims, lat.spacing, lat.origin, bs, rc)
+    nbx, nby, nbz = bd
+    nbins = nbx * nby * nbz
+    print(f"[max atoms] n={n} dims={lat.dims} bins={bd}", flush=True)
+    chunk = 1 << 27
+    gen = torch.Generator(device="cuda").manual_seed(58)
+    atoms = torch.empty((n, 4), dtype=torch.float32, device="cuda")
+    lo = torch.tensor(b0 + 0.01, dtype=torch.float32, device="cuda")
+    span = torch.tensor(np.asarray(bd, np.float32) * bs - 0.02, dtype=torch.float32,
+                        device="cuda")
+    ai = atoms.view(torch.int32)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        atoms[s:e, :3] = lo + torch.rand((e - s, 3), generator=gen, device="cuda") * span
+        ai[s:e, 3] = torch.arange(s, e, dtype=torch.int32, device="cuda")
+    atoms[7::1000, 0] = 1.0e30
+    kept = n - len(range(7, n, 1000))
+
+    ws = cpmap.bin_atoms(atoms, lat, bs, rc)
+    starts, srt = cpmap.workspace_views(ws, n, lat, bs, rc)
+    torch.cuda.synchronize()
+    print(f"[max atoms] binned n={n}", flush=True)
+    assert int(starts[0]) == 0 and int(starts[-1]) == kept
+    assert bool((starts[1:] >= starts[:-1]).all())
+    starts64 = starts.long()
+
+    # torch gathers from one tensor of fewer than 2^31 elements at a time:
+    # the input atoms' four words and the sorted atoms' index word as columns
+    si = srt.view(torch.int32)
+    cols = [ai[:, k].contiguous() for k in range(4)]
+    orig_all = si[:, 3].contiguous()
+    seen = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    b0_64 = torch.tensor(b0.astype(np.float64), device="cuda")
+    slack = 2.0 ** -20 * float(max(bd))  # far above the fp32 bin coordinate's error
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        e1 = min(n, e + 1)  # one position past the chunk, for the order check
+        orig = orig_all[s:e1].long()
+        assert int(orig.min()) >= 0 and int(orig.max()) < n
+        seen[orig[:e - s]] = 1
+        for k in range(4):
+            assert bool((cols[k].index_select(0, orig[:e - s]) == si[s:e, k]).all()), \
+                f"word {k} of the atoms in [{s}, {e})"
+        bins = _positions_bins(torch, starts64, kept, nbins, s, e1)
+        same = bins[1:] == bins[:-1]
+        assert bool((~same | (orig[1:] > orig[:-1])).all()), f"input order in [{s}, {e1})"
+        is_kept = bins[:e - s] < nbins
+        t = (srt[s:e, :3].double() - b0_64) / bs
+        c = torch.stack([bins[:e - s] % nbx, (bins[:e - s] // nbx) % nby,
+                         bins[:e - s] // (nbx * nby)], dim=1).double()
+        inside = ((t >= c - slack) & (t < c + 1 + slack)).all(dim=1)
+        assert bool((inside | ~is_kept).all()), f"bin boxes in [{s}, {e})"
+        assert bool(((srt[s:e, 0] == 1.0e30) | is_kept).all()), f"dropped atoms in [{s}, {e})"
+    assert bool(seen.all())
+    del seen
+
+    rng = np.random.default_rng(59)
+    picks = np.unique(np.concatenate([
+        np.arange(0, 1 << 16), np.arange(n - (1 << 16), n),
+        np.arange(kept - 512, min(n, kept + 512)),
+        rng.integers(0, n, size=100_000)]).astype(np.int64))
+    orig = orig_all.index_select(0, torch.from_numpy(picks).cuda()).long()
+    sample = torch.stack([cols[k].index_select(0, orig) for k in range(4)], dim=1)
+    sample = sample.view(torch.float32).cpu().numpy()
+    _, _, bin_of = oracle.bin_atoms(sample, lat.dims, lat.spacing, lat.origin, bs, rc)
+    st = starts.cpu().numpy().astype(np.int64)
+    ok = np.where(bin_of >= 0,
+                  (st[np.maximum(bin_of, 0)] <= picks) & (picks < st[np.maximum(bin_of, 0) + 1]),
+                  picks >= kept)
+    assert ok.all(), f"{(~ok).sum()} sampled positions outside their oracle bin"
+    del atoms, ws, starts, srt, starts64, si, ai, cols, orig_all, orig
