@@ -240,3 +240,29 @@ def test_bin_atoms_at_the_largest_atom_count(torch, free_after, n):
                   picks >= kept)
     assert ok.all(), f"{(~ok).sum()} sampled positions outside their oracle bin"
     del atoms, ws, starts, srt, starts64, si, ai, cols, orig_all, orig
+
+
+def test_direct_at_the_largest_atom_count(torch, free_after):
+    """n_atoms = CPMAP_MAX_ATOMS (2^31 - 1) on a two-node lattice, with the
+    atom split the library plans (32 parts of 16 waves): every part's and
+    wave's atom slice, and the last atom index, reach the top of int32.
+    Parity with the fp64 oracle at both nodes, under the usual bound."""
+    n = 2**31 - 1
+    lat = Lattice(2, 1, 1, 0.5)
+    print(f"[max atoms direct] n={n} dims={lat.dims} plan={cpmap.direct_plan(n, lat)}",
+          flush=True)
+    gen = torch.Generator(device="cuda").manual_seed(60)
+    atoms = torch.empty((n, 4), dtype=torch.float32, device="cuda")
+    chunk = 1 << 27
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        u = torch.rand((e - s, 4), generator=gen, device="cuda")
+        atoms[s:e, :3] = u[:, :3] * 40.0 - 20.0
+        atoms[s:e, 3] = u[:, 3] * 2.0 - 1.0
+    V = cpmap.direct(atoms, lat)
+    Vg = V.view(-1).cpu().numpy()
+    atoms_np = atoms.cpu().numpy()
+    del atoms, V
+    print("[max atoms direct] oracle", flush=True)
+    Vo, S = oracle.direct(atoms_np, lat.dims, lat.spacing, lat.origin, with_scale=True)
+    _parity(Vg, Vo, S, "direct at 2^31 - 1 atoms")
