@@ -605,10 +605,12 @@ cutoff_kernel(CutoffParams P0, const WorkspaceHeader *__restrict__ hdr,
 
         // 3. stage the spans' atoms in chunks; each cube lists the atoms near
         //    its nodes and its lanes sweep them
-        for (int32_t c0 = 0; c0 < total; c0 += kStage) {
-            const int32_t m = total - c0 < kStage ? total - c0 : kStage;
+        // (64-bit chunk start: a neighbourhood can hold up to 2^31 - 1 atoms,
+        // and the step past the last chunk must not wrap)
+        for (int64_t c0 = 0; c0 < total; c0 += kStage) {
+            const int32_t m = total - c0 < kStage ? (int32_t)(total - c0) : kStage;
             for (int32_t e = t; e < m; e += kThreads) {
-                const int32_t g = c0 + e;
+                const int32_t g = (int32_t)(c0 + e);
                 int32_t a = 0, b = rows;  // last row with span_off[row] <= g
                 while (b - a > 1) {
                     const int32_t mid = (a + b) >> 1;

@@ -266,3 +266,44 @@ def test_direct_at_the_largest_atom_count(torch, free_after):
     print("[max atoms direct] oracle", flush=True)
     Vo, S = oracle.direct(atoms_np, lat.dims, lat.spacing, lat.origin, with_scale=True)
     _parity(Vg, Vo, S, "direct at 2^31 - 1 atoms")
+
+
+def test_cutoff_neighbourhood_of_2_31_atoms(torch, free_after):
+    """One tile whose bin neighbourhood holds all 2^31 - 1 atoms (an 8x8x8
+    lattice, 4 A bins, rc = 2 A: the 3x3x3 bins around it), so the staging
+    loop's last chunk starts at 2^31 - 256.  All but 64 atoms lie more than
+    rc from every node (they are staged and tested, never summed); the 64
+    near ones come last in input order and in the last bin, so they sit in
+    that final chunk.  Atoms beyond rc add nothing to the smoothed term, so
+    the oracle on the near atoms is the oracle on all of them."""
+    n, n_near = 2**31 - 1, 64
+    lat, bs, rc = Lattice(8, 8, 8, 0.5), 4.0, 2.0  # nodes in [0, 3.5]^3, bins from -4 to 8
+    print(f"[max neighbourhood] n={n} dims={lat.dims} bins={cpmap.bin_grid(lat, bs, rc)}",
+          flush=True)
+    gen = torch.Generator(device="cuda").manual_seed(61)
+    atoms = torch.empty((n, 4), dtype=torch.float32, device="cuda")
+    n_far = n - n_near
+    chunk = 1 << 27
+    for s in range(0, n_far, chunk):
+        e = min(n_far, s + chunk)
+        u = torch.rand((e - s, 5), generator=gen, device="cuda")
+        # x in [-3.99, -2.2] or [5.7, 7.99]: at least 2.2 A from the node box
+        x = torch.where(u[:, 4] < 0.5, -3.99 + u[:, 0] * 1.79, 5.7 + u[:, 0] * 2.29)
+        atoms[s:e, 0] = x
+        atoms[s:e, 1:3] = -3.99 + u[:, 1:3] * 11.98
+        atoms[s:e, 3] = u[:, 3] * 2.0 - 1.0
+        assert float(x.abs().min()) >= 2.2 - 1e-6 and float((x - 3.5).abs().min()) >= 2.2 - 1e-6
+    near = wl.random_atoms(n_near, (4.05, 4.05, 4.05), (4.6, 4.6, 4.6), seed=62)
+    atoms[n_far:] = torch.from_numpy(near).cuda()
+    ws = cpmap.bin_atoms(atoms, lat, bs, rc)
+    starts, srt = cpmap.workspace_views(ws, n, lat, bs, rc)
+    # every atom is kept, and the near ones are the sorted array's last 64
+    assert int(starts[-1]) == n
+    assert torch.equal(srt[n_far:].cpu(), torch.from_numpy(near))
+    print("[max neighbourhood] binned; cutoff", flush=True)
+    V = cpmap.cutoff(ws, n, lat, bs, rc)
+    Vg = V.view(-1).cpu().numpy()
+    del atoms, ws, starts, srt, V
+    Vo, S = oracle.cutoff(near, lat.dims, lat.spacing, lat.origin, rc, with_scale=True)
+    assert np.count_nonzero(S) > 0
+    _parity(Vg, Vo, S, "cutoff with 2^31 - 1 atoms in one neighbourhood")
