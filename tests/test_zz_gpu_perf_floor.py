@@ -1,5 +1,5 @@
 """Speed floors for the hot paths at the benchmark sizes, set well below
-what they measure (the direct map takes 165 ms with its workspace and 180 ms
+what they measure (the direct map takes 156 ms with its workspace and 171 ms
 without, the cutoff map 1.45 ms smoothed and 1.37 ms truncated, the extrema
 of the 200^3 map 15-17 us per event-timed call, the k = 10 plane 28-30 us),
 so that they only trip on a real regression (a spilling build, a lost
