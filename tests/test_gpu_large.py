@@ -37,6 +37,14 @@ def free_after(torch):
     torch.cuda.empty_cache()
 
 
+def _need_free_gb(torch, gb):
+    """Skip (with the reason) when the device lacks the free memory a
+    maximum-size case needs, rather than failing on allocation."""
+    free, _ = torch.cuda.mem_get_info()
+    if free < gb * 2**30:
+        pytest.skip(f"needs {gb} GiB of free device memory, {free / 2**30:.0f} GiB free")
+
+
 def _linear(lat, i, j, k):
     return (np.asarray(k, np.int64) * lat.ny + np.asarray(j, np.int64)) * lat.nx + np.asarray(i, np.int64)
 
@@ -169,6 +177,7 @@ def test_bin_atoms_at_the_largest_atom_count(torch, free_after, n):
     bins keep input order.  At sampled positions the oracle's own bin of the
     input atom must contain the position."""
     lat, bs, rc = Lattice(200, 200, 200, 0.5), 1.0, 3.0  # 106^3 bins: 3 radix passes
+    _need_free_gb(torch, 1 + n * 80 / 2**30)  # atoms, workspace, column copies, chunks
     bd, b0, _ = oracle.bin_grid(lat.dims, lat.spacing, lat.origin, bs, rc)
     nbx, nby, nbz = bd
     nbins = nbx * nby * nbz
@@ -249,6 +258,7 @@ def test_direct_at_the_largest_atom_count(torch, free_after):
     Parity with the fp64 oracle at both nodes, under the usual bound."""
     n = 2**31 - 1
     lat = Lattice(2, 1, 1, 0.5)
+    _need_free_gb(torch, 40)
     print(f"[max atoms direct] n={n} dims={lat.dims} plan={cpmap.direct_plan(n, lat)}",
           flush=True)
     gen = torch.Generator(device="cuda").manual_seed(60)
@@ -278,6 +288,7 @@ def test_cutoff_neighbourhood_of_2_31_atoms(torch, free_after):
     the oracle on the near atoms is the oracle on all of them."""
     n, n_near = 2**31 - 1, 64
     lat, bs, rc = Lattice(8, 8, 8, 0.5), 4.0, 2.0  # nodes in [0, 3.5]^3, bins from -4 to 8
+    _need_free_gb(torch, 110)
     print(f"[max neighbourhood] n={n} dims={lat.dims} bins={cpmap.bin_grid(lat, bs, rc)}",
           flush=True)
     gen = torch.Generator(device="cuda").manual_seed(61)
