@@ -485,3 +485,32 @@ def test_reused_workspace_memory_is_refused_or_nan(torch):
         torch.cuda.synchronize()
         assert ws2.data_ptr() == addr
         assert torch.isnan(V).all().item()
+
+
+FAR = (8192.5, -4096.25, 2048.125)
+
+
+@pytest.mark.parametrize("term", ["smoothed", "truncated"])
+def test_far_from_the_origin(torch, term):
+    """A lattice some 10^4 A from the origin, where an fp32 coordinate keeps
+    about three decimal digits after the point: binning bit-exact, and both
+    cutoff terms and the direct sum (plain and split) within the bound at
+    every node."""
+    lat = Lattice(33, 17, 9, 0.5, FAR)
+    lo = (FAR[0] - 6.0, FAR[1] - 6.0, FAR[2] - 6.0)
+    hi = (FAR[0] + 22.0, FAR[1] + 14.0, FAR[2] + 10.0)
+    n, bs, rc = 1500, 2.0, 5.0
+    print(f"[far origin] origin={FAR} dims={lat.dims} term={term}", flush=True)
+    atoms_np = wl.random_atoms(n, lo, hi, seed=63)
+    _check_csr(torch, atoms_np, lat, bs, rc)
+    atoms = torch.from_numpy(atoms_np).cuda()
+    ws = cpmap.bin_atoms(atoms, lat, bs, rc)
+    V = cpmap.cutoff(ws, n, lat, bs, rc, term=term).cpu().numpy().reshape(-1)
+    ref = oracle.cutoff if term == "smoothed" else oracle.cutoff_hard
+    Vo, S = ref(atoms_np, lat.dims, lat.spacing, lat.origin, rc, with_scale=True)
+    assert np.count_nonzero(S) > lat.n_points // 2
+    _parity(V, Vo, S, f"far origin, {term}")
+    Vdo, Sd = oracle.direct(atoms_np, lat.dims, lat.spacing, lat.origin, with_scale=True)
+    for split in (False, True):
+        Vd = cpmap.direct(atoms, lat, split=split).cpu().numpy().reshape(-1)
+        _parity(Vd, Vdo, Sd, f"far origin, direct split={split}")
